@@ -1,0 +1,198 @@
+"""Python binding of libuocr_sparse.so, the SR-SWA block-sparse attention hot
+path for MI355X (gfx950).
+
+Argument marshalling only: every function forwards to the C entry point of
+the same name (``uocr_<name>`` in ``include/uocr_sparse.h``) and raises
+``UocrError`` on a non-zero status.  Tensor arguments are ``torch.Tensor``s on
+the GPU (their ``data_ptr()`` is passed) or raw integer device pointers; the
+stream defaults to torch's current stream.  There is no fallback: importing
+this package without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = [
+    "SparseCfg", "KV", "UocrError", "lib_path", "make_cfg", "make_kv",
+    "indexer_score_decode", "block_topk_decode", "sparse_attn_decode",
+    "indexer_score_prefill", "block_topk_prefill", "sparse_attn_prefill",
+    "workspace_size", "status_string", "last_error", "abi_version",
+    "OP_INDEXER_DECODE", "OP_TOPK_DECODE", "OP_ATTN_DECODE",
+    "OP_INDEXER_PREFILL", "OP_TOPK_PREFILL", "OP_ATTN_PREFILL",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libuocr_sparse.so")
+
+OP_INDEXER_DECODE, OP_TOPK_DECODE, OP_ATTN_DECODE = 0, 1, 2
+OP_INDEXER_PREFILL, OP_TOPK_PREFILL, OP_ATTN_PREFILL = 3, 4, 5
+
+
+class SparseCfg(ctypes.Structure):
+    """Mirror of ``uocr_sparse_cfg``."""
+    _fields_ = [
+        ("block_size", ctypes.c_int32),
+        ("topk_blocks", ctypes.c_int32),
+        ("local_blocks", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("index_dim", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+    ]
+
+
+class KV(ctypes.Structure):
+    """Mirror of ``uocr_kv`` (one layer's block-major cache)."""
+    _fields_ = [
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("kidx_pool", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("ctx_lens", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int64),
+        ("batch", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+    ]
+
+
+class UocrError(RuntimeError):
+    def __init__(self, status: int, func: str):
+        self.status = status
+        msg = _lib.uocr_last_error().decode(errors="replace")
+        super().__init__(f"{func}: {_lib.uocr_status_string(status).decode()}: {msg}")
+
+
+if not os.path.exists(lib_path):
+    raise ImportError(
+        f"{lib_path} is missing: build it with `python -m block_sparse_long_sr_amd.build` "
+        "(there is no CPU fallback)")
+
+_lib = ctypes.CDLL(lib_path)
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_CFG = ctypes.POINTER(SparseCfg)
+_KV = ctypes.POINTER(KV)
+
+_SIGS = {
+    "uocr_indexer_score_decode": ([_CFG, _KV, _P, _P, _P], ctypes.c_int),
+    "uocr_block_topk_decode": ([_CFG, _P, _P, _I32, _I32, _P, _P, _P], ctypes.c_int),
+    "uocr_sparse_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "uocr_indexer_score_prefill": ([_CFG, _KV, _P, _I32, _I32, _P, _SZ, _P], ctypes.c_int),
+    "uocr_block_topk_prefill": ([_CFG, _P, _SZ, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
+    "uocr_sparse_attn_prefill": ([_CFG, _KV, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "uocr_workspace_size": ([_CFG, _I32, _I32, _I32], ctypes.c_size_t),
+    "uocr_status_string": ([_I32], ctypes.c_char_p),
+    "uocr_last_error": ([], ctypes.c_char_p),
+    "uocr_abi_version": ([], ctypes.c_int32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+
+def _ptr(x) -> Optional[int]:
+    """Device address of a tensor, an int pointer, or a (pointer, bytes) pair."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, tuple):
+        return int(x[0])
+    if not x.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous (the C ABI takes dense row-major buffers)")
+    return x.data_ptr()
+
+
+def _nbytes(x) -> int:
+    """Byte size of a workspace given as a tensor or a (pointer, bytes) pair."""
+    if x is None:
+        return 0
+    if isinstance(x, tuple):
+        return int(x[1])
+    if isinstance(x, int):
+        raise TypeError("pass a workspace as a tensor or a (pointer, bytes) pair")
+    return x.numel() * x.element_size()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, func: str) -> None:
+    if status != 0:
+        raise UocrError(status, func)
+
+
+def make_cfg(topk_blocks: int = 16, local_blocks: int = 4, num_heads: int = 10, head_dim: int = 128,
+             index_dim: int = 128, block_size: int = 32, sm_scale: Optional[float] = None) -> SparseCfg:
+    """Configuration with the released model's defaults (32 / 16 / 4 / 10 x 128)."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(head_dim)
+    return SparseCfg(block_size, topk_blocks, local_blocks, num_heads, head_dim, index_dim, sm_scale)
+
+
+def make_kv(k_pool, v_pool, kidx_pool, block_table, ctx_lens, num_blocks: int, batch: int, max_blocks: int) -> KV:
+    return KV(_ptr(k_pool), _ptr(v_pool), _ptr(kidx_pool), _ptr(block_table), _ptr(ctx_lens),
+              int(num_blocks), int(batch), int(max_blocks))
+
+
+def indexer_score_decode(cfg: SparseCfg, kv: KV, q_idx, block_scores, stream=None) -> None:
+    _check(_lib.uocr_indexer_score_decode(ctypes.byref(cfg), ctypes.byref(kv), _ptr(q_idx), _ptr(block_scores),
+                                          _stream(stream)), "indexer_score_decode")
+
+
+def block_topk_decode(cfg: SparseCfg, block_scores, ctx_lens, batch: int, max_blocks: int, block_idx,
+                      n_sel=None, stream=None) -> None:
+    _check(_lib.uocr_block_topk_decode(ctypes.byref(cfg), _ptr(block_scores), _ptr(ctx_lens), batch, max_blocks,
+                                       _ptr(block_idx), _ptr(n_sel), _stream(stream)), "block_topk_decode")
+
+
+def sparse_attn_decode(cfg: SparseCfg, kv: KV, q, block_idx, out, lse=None, ws=None, stream=None) -> None:
+    _check(_lib.uocr_sparse_attn_decode(ctypes.byref(cfg), ctypes.byref(kv), _ptr(q), _ptr(block_idx), _ptr(out),
+                                        _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream)), "sparse_attn_decode")
+
+
+def indexer_score_prefill(cfg: SparseCfg, kv: KV, q_idx, q_start: int, T: int, cand_ws, stream=None) -> None:
+    _check(_lib.uocr_indexer_score_prefill(ctypes.byref(cfg), ctypes.byref(kv), _ptr(q_idx), q_start, T,
+                                           _ptr(cand_ws), _nbytes(cand_ws), _stream(stream)),
+           "indexer_score_prefill")
+
+
+def block_topk_prefill(cfg: SparseCfg, cand_ws, q_start: int, T: int, max_blocks: int, block_idx, n_sel=None,
+                       stream=None) -> None:
+    _check(_lib.uocr_block_topk_prefill(ctypes.byref(cfg), _ptr(cand_ws), _nbytes(cand_ws), q_start, T, max_blocks,
+                                        _ptr(block_idx), _ptr(n_sel), _stream(stream)), "block_topk_prefill")
+
+
+def sparse_attn_prefill(cfg: SparseCfg, kv: KV, q, q_start: int, T: int, block_idx, out, lse=None, ws=None,
+                        stream=None) -> None:
+    _check(_lib.uocr_sparse_attn_prefill(ctypes.byref(cfg), ctypes.byref(kv), _ptr(q), q_start, T, _ptr(block_idx),
+                                         _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "sparse_attn_prefill")
+
+
+def workspace_size(cfg: SparseCfg, op: int, rows: int, max_blocks: int) -> int:
+    return int(_lib.uocr_workspace_size(ctypes.byref(cfg), op, rows, max_blocks))
+
+
+def status_string(status: int) -> str:
+    return _lib.uocr_status_string(status).decode()
+
+
+def last_error() -> str:
+    return _lib.uocr_last_error().decode(errors="replace")
+
+
+def abi_version() -> int:
+    return int(_lib.uocr_abi_version())

@@ -1,0 +1,76 @@
+"""Build libuocr_sparse.so (gfx950) in-tree with hipcc.
+
+Usage: ``python -m block_sparse_long_sr_amd.build`` or ``build()``.  Every call
+recompiles every source; the objects go to ``_build/`` and the shared library
+next to this file, where the binding loads it.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB_NAME = "libuocr_sparse.so"
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# Packed fp32 VALU forms are kept out of generated code (-packed-fp32-ops);
+# the host pass reports the feature as unknown, which is harmless.
+DEVICE_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-munsafe-fp-atomics",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC"]
+
+SOURCES = ["api.cpp", "indexer_decode.hip", "topk_decode.hip", "attn.hip", "indexer_prefill.hip"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def compile_objects(sources, src_dir, obj_dir, extra=()):
+    os.makedirs(obj_dir, exist_ok=True)
+    jobs = []
+    for s in sources:
+        src = os.path.join(src_dir, s)
+        obj = os.path.join(obj_dir, os.path.splitext(s)[0] + ".o")
+        if s.endswith(".hip"):
+            cmd = [HIPCC, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
+        else:
+            cmd = [HIPCC, *HOST_FLAGS, *extra, "-c", src, "-o", obj]
+        jobs.append((cmd, obj))
+    workers = min(len(jobs), max(1, min(8, (os.cpu_count() or 2))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        outs = list(ex.map(lambda j: _run(j[0]), jobs))
+    return [o for _, o in jobs], outs
+
+
+def link(objs, out_path):
+    tmp = out_path + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, out_path)
+
+
+def build(verbose: bool = False) -> str:
+    objs, outs = compile_objects(SOURCES, CSRC, os.path.join(ROOT, "_build", "uocr_sparse"))
+    lib = os.path.join(PKG, LIB_NAME)
+    link(objs, lib)
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+        print(f"built {lib}")
+    return lib
+
+
+if __name__ == "__main__":
+    build(verbose="-q" not in sys.argv)

@@ -1,0 +1,301 @@
+// C ABI of the SR-SWA hot path: host-side argument checks, then kernel
+// launches.  No HIP call is made before every check of a call has passed, so
+// the checks run (and are tested) on machines without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/uocr_sparse.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return UOCR_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int32_t kMaxTopk = 4096;
+constexpr int32_t kMaxBatch = 65535;
+constexpr int32_t kMaxBlocks = 1 << 20;
+constexpr int32_t kMaxHeads = 64;
+constexpr int32_t kMaxRemotePrefill = 16;
+
+int check_cfg(const uocr_sparse_cfg* c) {
+  if (c == nullptr) return fail(UOCR_EINVAL, "cfg is NULL");
+  if (c->block_size != 32) return fail(UOCR_EINVAL, "block_size must be 32 (got %d)", c->block_size);
+  if (c->head_dim != 128) return fail(UOCR_EINVAL, "head_dim must be 128 (got %d)", c->head_dim);
+  if (c->index_dim != 128) return fail(UOCR_EINVAL, "index_dim must be 128 (got %d)", c->index_dim);
+  if (c->local_blocks < 1) return fail(UOCR_EINVAL, "local_blocks must be >= 1 (got %d)", c->local_blocks);
+  if (c->topk_blocks < c->local_blocks || c->topk_blocks > kMaxTopk)
+    return fail(UOCR_EINVAL, "topk_blocks must be in [local_blocks, %d] (got %d, local %d)", kMaxTopk,
+                c->topk_blocks, c->local_blocks);
+  if (c->num_heads < 1 || c->num_heads > kMaxHeads)
+    return fail(UOCR_EINVAL, "num_heads must be in [1, %d] (got %d)", kMaxHeads, c->num_heads);
+  if (!std::isfinite(c->sm_scale) || !(c->sm_scale > 0.0f))
+    return fail(UOCR_EINVAL, "sm_scale must be finite and > 0");
+  return UOCR_OK;
+}
+
+int check_dims(int32_t batch, int32_t max_blocks) {
+  if (batch < 0 || batch > kMaxBatch) return fail(UOCR_ESHAPE, "batch must be in [0, %d] (got %d)", kMaxBatch, batch);
+  if (max_blocks < 1 || max_blocks > kMaxBlocks)
+    return fail(UOCR_ESHAPE, "max_blocks must be in [1, %d] (got %d)", kMaxBlocks, max_blocks);
+  return UOCR_OK;
+}
+
+#define REQ_PTR16(p, name)                                                             \
+  do {                                                                                 \
+    if ((p) == nullptr) return fail(UOCR_EINVAL, "%s is NULL", name);                  \
+    if (!aligned16(p)) return fail(UOCR_EINVAL, "%s is not 16-byte aligned", name);    \
+  } while (0)
+#define REQ_PTR4(p, name)                                                              \
+  do {                                                                                 \
+    if ((p) == nullptr) return fail(UOCR_EINVAL, "%s is NULL", name);                  \
+    if (!aligned4(p)) return fail(UOCR_EINVAL, "%s is not 4-byte aligned", name);      \
+  } while (0)
+#define OPT_PTR4(p, name)                                                              \
+  do {                                                                                 \
+    if ((p) != nullptr && !aligned4(p)) return fail(UOCR_EINVAL, "%s is not 4-byte aligned", name); \
+  } while (0)
+#define TRY(expr)                  \
+  do {                             \
+    int _rc = (expr);              \
+    if (_rc != UOCR_OK) return _rc; \
+  } while (0)
+
+int check_kv(const uocr_kv* kv, bool need_kidx, bool need_kv) {
+  if (kv == nullptr) return fail(UOCR_EINVAL, "kv is NULL");
+  TRY(check_dims(kv->batch, kv->max_blocks));
+  if (kv->batch == 0) return UOCR_OK;
+  if (kv->num_blocks < 1) return fail(UOCR_ESHAPE, "kv->num_blocks must be >= 1");
+  if (need_kidx) REQ_PTR16(kv->kidx_pool, "kv->kidx_pool");
+  if (need_kv) {
+    REQ_PTR16(kv->k_pool, "kv->k_pool");
+    REQ_PTR16(kv->v_pool, "kv->v_pool");
+  }
+  REQ_PTR4(kv->block_table, "kv->block_table");
+  return UOCR_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(UOCR_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int check_prefill_range(const uocr_kv* kv, int32_t q_start, int32_t T) {
+  if (kv->batch != 1) return fail(UOCR_ESHAPE, "prefill needs kv->batch == 1 (got %d)", kv->batch);
+  if (q_start < 0) return fail(UOCR_ESHAPE, "q_start must be >= 0 (got %d)", q_start);
+  if (T < 0) return fail(UOCR_ESHAPE, "T must be >= 0 (got %d)", T);
+  if ((int64_t)q_start + T > (int64_t)kv->max_blocks * 32)
+    return fail(UOCR_ESHAPE, "q_start + T (%lld) exceeds 32 * max_blocks (%lld)", (long long)q_start + T,
+                (long long)kv->max_blocks * 32);
+  return UOCR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int uocr_indexer_score_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q_idx,
+                              float* block_scores, void* stream) {
+  TRY(check_cfg(cfg));
+  TRY(check_kv(kv, true, false));
+  if (kv->batch == 0) return ok();
+  REQ_PTR4(kv->ctx_lens, "kv->ctx_lens");
+  REQ_PTR16(q_idx, "q_idx");
+  REQ_PTR4(block_scores, "block_scores");
+  uocr::IndexerDecodeArgs a{};
+  a.kidx_pool = kv->kidx_pool;
+  a.block_table = kv->block_table;
+  a.ctx_lens = kv->ctx_lens;
+  a.q_idx = q_idx;
+  a.block_scores = block_scores;
+  a.num_blocks = kv->num_blocks;
+  a.batch = kv->batch;
+  a.max_blocks = kv->max_blocks;
+  a.local_blocks = cfg->local_blocks;
+  a.chunk = uocr::indexer_decode_chunk(kv->batch, kv->max_blocks);
+  return hip_status(uocr::launch_indexer_decode(a, static_cast<hipStream_t>(stream)), "indexer_score_decode");
+}
+
+int uocr_block_topk_decode(const uocr_sparse_cfg* cfg, const float* block_scores, const int32_t* ctx_lens,
+                           int32_t batch, int32_t max_blocks, int32_t* block_idx, int32_t* n_sel, void* stream) {
+  TRY(check_cfg(cfg));
+  TRY(check_dims(batch, max_blocks));
+  if (batch == 0) return ok();
+  REQ_PTR4(block_scores, "block_scores");
+  REQ_PTR4(ctx_lens, "ctx_lens");
+  REQ_PTR4(block_idx, "block_idx");
+  OPT_PTR4(n_sel, "n_sel");
+  uocr::TopkDecodeArgs a{};
+  a.block_scores = block_scores;
+  a.ctx_lens = ctx_lens;
+  a.block_idx = block_idx;
+  a.n_sel = n_sel;
+  a.batch = batch;
+  a.max_blocks = max_blocks;
+  a.topk = cfg->topk_blocks;
+  a.local_blocks = cfg->local_blocks;
+  return hip_status(uocr::launch_topk_decode(a, static_cast<hipStream_t>(stream)), "block_topk_decode");
+}
+
+static int attn_common(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q, const int32_t* block_idx,
+                       float* out, float* lse, int32_t nq, int prefill, int32_t q_start, void* stream) {
+  REQ_PTR16(q, "q");
+  REQ_PTR4(block_idx, "block_idx");
+  REQ_PTR4(out, "out");
+  OPT_PTR4(lse, "lse");
+  uocr::AttnArgs a{};
+  a.k_pool = kv->k_pool;
+  a.v_pool = kv->v_pool;
+  a.block_table = kv->block_table;
+  a.ctx_lens = kv->ctx_lens;
+  a.q = q;
+  a.block_idx = block_idx;
+  a.out = out;
+  a.lse = lse;
+  a.num_blocks = kv->num_blocks;
+  a.nq = nq;
+  a.heads = cfg->num_heads;
+  a.max_blocks = kv->max_blocks;
+  a.topk = cfg->topk_blocks;
+  a.scale_log2 = cfg->sm_scale * 1.44269504088896340736f;
+  a.prefill = prefill;
+  a.q_start = q_start;
+  return hip_status(uocr::launch_attn(a, static_cast<hipStream_t>(stream)),
+                    prefill ? "sparse_attn_prefill" : "sparse_attn_decode");
+}
+
+int uocr_sparse_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q,
+                            const int32_t* block_idx, float* out, float* lse, void* ws, size_t ws_bytes,
+                            void* stream) {
+  (void)ws;
+  (void)ws_bytes;  // this implementation needs no workspace (size query returns 0)
+  TRY(check_cfg(cfg));
+  TRY(check_kv(kv, false, true));
+  if (kv->batch == 0) return ok();
+  REQ_PTR4(kv->ctx_lens, "kv->ctx_lens");
+  return attn_common(cfg, kv, q, block_idx, out, lse, kv->batch, 0, 0, stream);
+}
+
+int uocr_indexer_score_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q_idx,
+                               int32_t q_start, int32_t T, void* cand_ws, size_t cand_ws_bytes, void* stream) {
+  TRY(check_cfg(cfg));
+  TRY(check_kv(kv, true, false));
+  TRY(check_prefill_range(kv, q_start, T));
+  if (cfg->topk_blocks - cfg->local_blocks > kMaxRemotePrefill)
+    return fail(UOCR_EUNSUPPORTED, "prefill supports topk_blocks - local_blocks <= %d (got %d)", kMaxRemotePrefill,
+                cfg->topk_blocks - cfg->local_blocks);
+  const uocr::PrefillPlan plan = uocr::prefill_plan(T, kv->max_blocks, cfg->topk_blocks, cfg->local_blocks);
+  if (T == 0 || plan.R == 0) return ok();
+  REQ_PTR16(q_idx, "q_idx");
+  if (cand_ws == nullptr) return fail(UOCR_EWORKSPACE, "cand_ws is NULL (%zu bytes needed)", plan.ws_bytes);
+  if (!aligned16(cand_ws)) return fail(UOCR_EINVAL, "cand_ws is not 16-byte aligned");
+  if (cand_ws_bytes < plan.ws_bytes)
+    return fail(UOCR_EWORKSPACE, "cand_ws has %zu bytes, %zu needed", cand_ws_bytes, plan.ws_bytes);
+  uocr::IndexerPrefillArgs a{};
+  a.kidx_pool = kv->kidx_pool;
+  a.block_table = kv->block_table;
+  a.q_idx = q_idx;
+  a.cand_keys = reinterpret_cast<uint32_t*>(static_cast<char*>(cand_ws) + uocr::prefill_keys_offset());
+  a.cand_idx = reinterpret_cast<int32_t*>(static_cast<char*>(cand_ws) + uocr::prefill_idx_offset(plan, T));
+  a.num_blocks = kv->num_blocks;
+  a.T = T;
+  a.q_start = q_start;
+  a.max_blocks = kv->max_blocks;
+  a.local_blocks = cfg->local_blocks;
+  a.plan = plan;
+  return hip_status(uocr::launch_indexer_prefill(a, static_cast<hipStream_t>(stream)), "indexer_score_prefill");
+}
+
+int uocr_block_topk_prefill(const uocr_sparse_cfg* cfg, const void* cand_ws, size_t cand_ws_bytes, int32_t q_start,
+                            int32_t T, int32_t max_blocks, int32_t* block_idx, int32_t* n_sel, void* stream) {
+  TRY(check_cfg(cfg));
+  TRY(check_dims(1, max_blocks));
+  if (q_start < 0) return fail(UOCR_ESHAPE, "q_start must be >= 0 (got %d)", q_start);
+  if (T < 0) return fail(UOCR_ESHAPE, "T must be >= 0 (got %d)", T);
+  if ((int64_t)q_start + T > (int64_t)max_blocks * 32)
+    return fail(UOCR_ESHAPE, "q_start + T exceeds 32 * max_blocks");
+  if (cfg->topk_blocks - cfg->local_blocks > kMaxRemotePrefill)
+    return fail(UOCR_EUNSUPPORTED, "prefill supports topk_blocks - local_blocks <= %d", kMaxRemotePrefill);
+  if (T == 0) return ok();
+  REQ_PTR4(block_idx, "block_idx");
+  OPT_PTR4(n_sel, "n_sel");
+  const uocr::PrefillPlan plan = uocr::prefill_plan(T, max_blocks, cfg->topk_blocks, cfg->local_blocks);
+  if (plan.ws_bytes > 0) {
+    if (cand_ws == nullptr) return fail(UOCR_EWORKSPACE, "cand_ws is NULL (%zu bytes needed)", plan.ws_bytes);
+    if (!aligned16(cand_ws)) return fail(UOCR_EINVAL, "cand_ws is not 16-byte aligned");
+    if (cand_ws_bytes < plan.ws_bytes)
+      return fail(UOCR_EWORKSPACE, "cand_ws has %zu bytes, %zu needed", cand_ws_bytes, plan.ws_bytes);
+  }
+  uocr::TopkPrefillArgs a{};
+  a.cand_keys = reinterpret_cast<const uint32_t*>(static_cast<const char*>(cand_ws) + uocr::prefill_keys_offset());
+  a.cand_idx = reinterpret_cast<const int32_t*>(static_cast<const char*>(cand_ws) + uocr::prefill_idx_offset(plan, T));
+  a.block_idx = block_idx;
+  a.n_sel = n_sel;
+  a.T = T;
+  a.q_start = q_start;
+  a.topk = cfg->topk_blocks;
+  a.local_blocks = cfg->local_blocks;
+  a.plan = plan;
+  return hip_status(uocr::launch_topk_prefill(a, static_cast<hipStream_t>(stream)), "block_topk_prefill");
+}
+
+int uocr_sparse_attn_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q, int32_t q_start,
+                             int32_t T, const int32_t* block_idx, float* out, float* lse, void* ws, size_t ws_bytes,
+                             void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  TRY(check_cfg(cfg));
+  TRY(check_kv(kv, false, true));
+  TRY(check_prefill_range(kv, q_start, T));
+  if (T == 0) return ok();
+  return attn_common(cfg, kv, q, block_idx, out, lse, T, 1, q_start, stream);
+}
+
+size_t uocr_workspace_size(const uocr_sparse_cfg* cfg, int32_t op, int32_t rows, int32_t max_blocks) {
+  if (check_cfg(cfg) != UOCR_OK || rows < 0 || max_blocks < 1 || max_blocks > kMaxBlocks) return 0;
+  switch (op) {
+    case UOCR_OP_INDEXER_PREFILL:
+    case UOCR_OP_TOPK_PREFILL:
+      if (cfg->topk_blocks - cfg->local_blocks > kMaxRemotePrefill) return 0;
+      return uocr::prefill_plan(rows, max_blocks, cfg->topk_blocks, cfg->local_blocks).ws_bytes;
+    default:
+      return 0;
+  }
+}
+
+const char* uocr_status_string(int32_t status) {
+  switch (status) {
+    case UOCR_OK: return "UOCR_OK";
+    case UOCR_EINVAL: return "UOCR_EINVAL: invalid argument";
+    case UOCR_ESHAPE: return "UOCR_ESHAPE: size or offset out of range";
+    case UOCR_EWORKSPACE: return "UOCR_EWORKSPACE: workspace missing or too small";
+    case UOCR_EHIP: return "UOCR_EHIP: HIP launch error";
+    case UOCR_EUNSUPPORTED: return "UOCR_EUNSUPPORTED: configuration not supported";
+    default: return "unknown status";
+  }
+}
+
+const char* uocr_last_error(void) { return g_last_error; }
+
+int32_t uocr_abi_version(void) { return UOCR_ABI_VERSION; }
+
+}  // extern "C"

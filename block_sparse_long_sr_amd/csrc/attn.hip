@@ -1,0 +1,152 @@
+// Sparse gather attention over the kept blocks (SR-SWA step 4,
+// news.rkmt.cn/news/25027 Sec. 5): per head, exact softmax over the tokens of
+// the kept blocks that the query may see (token <= p), times V.  Decode and
+// chunked prefill share the kernel; a prefill row is a query of sequence 0
+// at p = q_start + row.
+//
+// One 512-thread workgroup per (query, head): the kept blocks are split over
+// its 8 waves (split-K), each wave keeps an online-softmax state (running
+// max, sum, 128-dim accumulator) and the waves' states are merged through LDS
+// at the end.  A wave reads a block's 8 KB K tile and 8 KB V tile with
+// contiguous 1 KB loads: lane l holds dims 8*(l%16)..+8 of keys 4k + l/16
+// (k = 0..7), which are exactly the keys whose probabilities it needs for its
+// V slice, so scores never leave the lane's DPP row.  Arithmetic is fp32
+// with exp2 on log2e-scaled logits; the output is fp32.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace uocr {
+
+namespace {
+constexpr int kAttnThreads = 512;
+constexpr int kAttnWaves = kAttnThreads / kWave;
+}  // namespace
+
+__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
+  __shared__ float s_m[kAttnWaves];
+  __shared__ float s_l[kAttnWaves];
+  __shared__ float s_o[kAttnWaves][kDim];
+
+  const int qi = blockIdx.x;
+  const int h = blockIdx.y;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int g = lane >> 4;        // key row group within a 4-key slab
+  const int c8 = (lane & 15) * 8; // first dim of the lane's slice
+
+  int seq, p;
+  if (a.prefill) {
+    seq = 0;
+    p = a.q_start + qi;
+  } else {
+    seq = qi;
+    p = clamp_ctx(a.ctx_lens[qi], a.max_blocks) - 1;
+  }
+  const int64_t head_row = (int64_t)qi * a.heads + h;
+  const uint4 qv = *reinterpret_cast<const uint4*>(a.q + head_row * kDim + c8);
+  const int32_t* sel = a.block_idx + (int64_t)qi * a.topk;
+  const int32_t* table = a.block_table + (int64_t)seq * a.max_blocks;
+
+  float m = -INFINITY;  // running max (log2 units), wave-uniform
+  float l = 0.0f;       // running sum over this lane's key group
+  float o[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) o[d] = 0.0f;
+
+  for (int e = wave; e < a.topk; e += kAttnWaves) {
+    const int j = __builtin_amdgcn_readfirstlane(sel[e]);
+    if (j < 0 || j >= a.max_blocks || j * kBlock > p) continue;
+    const int pb = __builtin_amdgcn_readfirstlane(table[j]);
+    if (pb < 0 || (int64_t)pb >= a.num_blocks) continue;
+    const int64_t tile = ((int64_t)pb * a.heads + h) * (kBlock * kDim);
+    const uint4* kt = reinterpret_cast<const uint4*>(a.k_pool + tile);
+    const uint4* vt = reinterpret_cast<const uint4*>(a.v_pool + tile);
+    uint4 kv[8], vv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) kv[k] = kt[k * kWave + lane];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) vv[k] = vt[k * kWave + lane];
+
+    const bool full = j * kBlock + (kBlock - 1) <= p;
+    float s[8];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float z = row16_sum(dot8_bf16(kv[k], qv)) * a.scale_log2;
+      if (!full && j * kBlock + 4 * k + g > p) z = -INFINITY;
+      s[k] = z;
+      bm = fmaxf(bm, z);
+    }
+    bm = fmaxf(bm, shfl_xor_f32(bm, 16));
+    bm = fmaxf(bm, shfl_xor_f32(bm, 32));
+    const float m_new = fmaxf(m, bm);
+    const float alpha = exp2f(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] *= alpha;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool valid = full || (j * kBlock + 4 * k + g <= p);
+      const float pk = valid ? exp2f(s[k] - m_new) : 0.0f;
+      l += pk;
+      if (valid) {
+        o[0] += pk * bf16_lo(vv[k].x);
+        o[1] += pk * bf16_hi(vv[k].x);
+        o[2] += pk * bf16_lo(vv[k].y);
+        o[3] += pk * bf16_hi(vv[k].y);
+        o[4] += pk * bf16_lo(vv[k].z);
+        o[5] += pk * bf16_hi(vv[k].z);
+        o[6] += pk * bf16_lo(vv[k].w);
+        o[7] += pk * bf16_hi(vv[k].w);
+      }
+    }
+    m = m_new;
+  }
+
+  // Sum the four key groups of the wave (lanes l, l^16, l^32, l^48).
+  l += shfl_xor_f32(l, 16);
+  l += shfl_xor_f32(l, 32);
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    o[d] += shfl_xor_f32(o[d], 16);
+    o[d] += shfl_xor_f32(o[d], 32);
+  }
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_l[wave] = l;
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) s_o[wave][c8 + d] = o[d];
+  }
+  __syncthreads();
+
+  if (threadIdx.x < kDim) {
+    const int d = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w]);
+    float res = 0.0f, lse_v = -INFINITY;
+    if (M != -INFINITY) {
+      float Lsum = 0.0f, acc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float f = exp2f(s_m[w] - M);
+        Lsum += s_l[w] * f;
+        acc += s_o[w][d] * f;
+      }
+      res = acc / Lsum;
+      lse_v = (M + log2f(Lsum)) * kLn2;
+    }
+    a.out[head_row * kDim + d] = res;
+    if (a.lse != nullptr && d == 0) a.lse[head_row] = lse_v;
+  }
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
+  if (a.nq == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_kernel, dim3(a.nq, a.heads), dim3(kAttnThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace uocr

@@ -1,0 +1,71 @@
+// Device helpers shared by the SR-SWA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace uocr {
+
+constexpr int kBlock = 32;     // tokens per KV block
+constexpr int kDim = 128;      // head_dim == index_dim
+constexpr int kWave = 64;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// c + a.lo*b.lo + a.hi*b.hi on two packed bf16 pairs (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+// Dot product of 8 bf16 pairs held as two uint4.
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b) {
+  float s = dot2_bf16(a.x, b.x, 0.0f);
+  s = dot2_bf16(a.y, b.y, s);
+  s = dot2_bf16(a.z, b.z, s);
+  return dot2_bf16(a.w, b.w, s);
+}
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
+// quad_perm [1,0,3,2] and [2,3,0,1] reduce each quad, row_half_mirror pairs
+// the two quads of each half row, row_mirror pairs the two halves.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return v;
+}
+
+__device__ __forceinline__ float shfl_xor_f32(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+// Order-preserving map float32 -> uint32: a > b (as numbers) <=> key(a) >
+// key(b); -0.0 maps like +0.0; NaN maps to 0, below every number.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (f != f) return 0u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ int clamp_ctx(int32_t L, int32_t max_blocks) {
+  const int hi = max_blocks * kBlock;
+  return L < 0 ? 0 : (L > hi ? hi : L);
+}
+
+}  // namespace uocr

@@ -1,0 +1,78 @@
+// Decode indexer scoring with fused block max (SR-SWA step 2,
+// news.rkmt.cn/news/25027 Sec. 5): for each sequence, every key of every
+// remote-candidate block is scored against the one-head 128-dim indexer
+// query, and each block keeps the maximum of its 32 key scores.
+//
+// The indexer-K cache is streamed once at HBM rate.  One wave scores one
+// 8 KB block: load k (k = 0..7) brings, in lane order, 1 KB = 4 key rows, so
+// lane l holds dims 8*(l%16)..+8 of key 4k + l/16 and every load instruction
+// reads a fully contiguous 1 KB.  The lane's 8-dim slice of the query stays
+// in registers; partial dots (v_dot2_f32_bf16, fp32 accumulate of exact
+// bf16 products) are summed over the 16 lanes of a DPP row, the block max is
+// taken in-lane over k and across the four rows with two xor shuffles.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace uocr {
+
+__global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerDecodeArgs a) {
+  const int b = blockIdx.y;
+  const int j0 = blockIdx.x * a.chunk;
+  if (j0 >= a.max_blocks) return;
+  const int L = clamp_ctx(a.ctx_lens[b], a.max_blocks);
+  const int nb = (L + kBlock - 1) / kBlock;
+  const int ncand = nb - a.local_blocks > 0 ? nb - a.local_blocks : 0;
+  const int jend_all = min(j0 + a.chunk, a.max_blocks);
+  float* out = a.block_scores + (int64_t)b * a.max_blocks;
+
+  // Non-candidate entries of this chunk (local, future, padding): -inf.
+  for (int j = max(j0, ncand) + (int)threadIdx.x; j < jend_all; j += blockDim.x) out[j] = -INFINITY;
+
+  const int jend = min(jend_all, ncand);
+  if (j0 >= jend) return;
+
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int nwaves = blockDim.x / kWave;
+  const uint4 qv = *reinterpret_cast<const uint4*>(a.q_idx + (int64_t)b * kDim + (lane & 15) * 8);
+  const int32_t* table = a.block_table + (int64_t)b * a.max_blocks;
+
+  for (int j = j0 + wave; j < jend; j += nwaves) {
+    const int pb = __builtin_amdgcn_readfirstlane(table[j]);
+    float score;
+    if (pb < 0 || (int64_t)pb >= a.num_blocks) {
+      score = __builtin_nanf("");
+    } else {
+      const uint4* base = reinterpret_cast<const uint4*>(a.kidx_pool + (int64_t)pb * (kBlock * kDim));
+      uint4 kv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) kv[k] = base[k * kWave + lane];
+      float m = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, row16_sum(dot8_bf16(kv[k], qv)));
+      m = fmaxf(m, shfl_xor_f32(m, 16));
+      m = fmaxf(m, shfl_xor_f32(m, 32));
+      score = m;
+    }
+    if (lane == 0) out[j] = score;
+  }
+}
+
+int32_t indexer_decode_chunk(int32_t batch, int32_t max_blocks) {
+  // Aim at ~2048 workgroups (8 per CU) so that enough 8 KB loads are in flight.
+  int64_t total = (int64_t)batch * max_blocks;
+  int64_t c = (total + 2047) / 2048;
+  if (c < 8) c = 8;
+  c = (c + 3) & ~int64_t(3);
+  if (c > max_blocks) c = max_blocks;
+  return (int32_t)c;
+}
+
+hipError_t launch_indexer_decode(const IndexerDecodeArgs& a, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  dim3 grid((a.max_blocks + a.chunk - 1) / a.chunk, a.batch);
+  hipLaunchKernelGGL(indexer_decode_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace uocr

@@ -1,0 +1,104 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by the caller and
+// returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace uocr {
+
+struct IndexerDecodeArgs {
+  const uint16_t* kidx_pool;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  const uint16_t* q_idx;
+  float* block_scores;
+  int64_t num_blocks;
+  int32_t batch;
+  int32_t max_blocks;
+  int32_t local_blocks;
+  int32_t chunk;  // blocks per workgroup
+};
+hipError_t launch_indexer_decode(const IndexerDecodeArgs& a, hipStream_t stream);
+int32_t indexer_decode_chunk(int32_t batch, int32_t max_blocks);
+
+struct TopkDecodeArgs {
+  const float* block_scores;
+  const int32_t* ctx_lens;
+  int32_t* block_idx;
+  int32_t* n_sel;
+  int32_t batch;
+  int32_t max_blocks;
+  int32_t topk;
+  int32_t local_blocks;
+};
+hipError_t launch_topk_decode(const TopkDecodeArgs& a, hipStream_t stream);
+
+struct AttnArgs {
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;  // decode only
+  const uint16_t* q;        // [nq][H][D]
+  const int32_t* block_idx; // [nq][topk]
+  float* out;               // [nq][H][D]
+  float* lse;               // [nq][H] or null
+  int64_t num_blocks;
+  int32_t nq;
+  int32_t heads;
+  int32_t max_blocks;
+  int32_t topk;
+  float scale_log2;         // sm_scale * log2(e)
+  int32_t prefill;          // 0: query i is sequence i at ctx_lens[i]-1; 1: row i of sequence 0 at q_start+i
+  int32_t q_start;
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+
+// Chunked-prefill scoring: partition of the context into splits.
+struct PrefillPlan {
+  int32_t n_tiles;   // ceil(T / 256) row tiles
+  int32_t bps;       // blocks per split
+  int32_t nsplit;    // splits (<= 64)
+  int32_t R;         // remote slots = topk - local
+  size_t ws_bytes;   // candidate workspace size
+};
+PrefillPlan prefill_plan(int32_t T, int32_t max_blocks, int32_t topk, int32_t local_blocks);
+
+struct IndexerPrefillArgs {
+  const uint16_t* kidx_pool;
+  const int32_t* block_table;  // row of sequence 0
+  const uint16_t* q_idx;       // [T][128]
+  uint32_t* cand_keys;         // [T][nsplit][R]
+  int32_t* cand_idx;           // [T][nsplit][R]
+  int64_t num_blocks;
+  int32_t T;
+  int32_t q_start;
+  int32_t max_blocks;
+  int32_t local_blocks;
+  PrefillPlan plan;
+};
+hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t stream);
+
+struct TopkPrefillArgs {
+  const uint32_t* cand_keys;
+  const int32_t* cand_idx;
+  int32_t* block_idx;  // [T][topk]
+  int32_t* n_sel;
+  int32_t T;
+  int32_t q_start;
+  int32_t topk;
+  int32_t local_blocks;
+  PrefillPlan plan;
+};
+hipError_t launch_topk_prefill(const TopkPrefillArgs& a, hipStream_t stream);
+
+// Layout of the opaque prefill candidate workspace.
+inline size_t prefill_keys_offset() { return 0; }
+inline size_t prefill_idx_offset(const PrefillPlan& p, int32_t T) {
+  size_t n = (size_t)T * (size_t)p.nsplit * (size_t)p.R * sizeof(uint32_t);
+  return (n + 255) & ~(size_t)255;
+}
+
+}  // namespace uocr

@@ -1,0 +1,221 @@
+/*
+ * uocr_sparse.h -- C ABI of the SR-SWA block-sparse attention hot path
+ * (gfx950 / MI355X).
+ *
+ * The method (news.rkmt.cn/news/25027, Unlimited-OCR-2 architecture
+ * walk-through, Sec. 5 "SR-SWA", steps 1-4; www.lqnn.cn/news/271890,
+ * KV-cache section):
+ *   1. cached keys are grouped in blocks of 32 tokens;
+ *   2. a one-head 128-dim indexer scores every cached key against the query
+ *      and a block scores the maximum of its keys;
+ *   3. each query keeps its 4 most recent ("local") blocks and the 12
+ *      highest-scoring earlier ("remote") blocks, 16 x 32 = 512 tokens;
+ *   4. exact causal softmax attention runs over the kept tokens only, 10
+ *      heads x 128 dims, K/V heads equal to query heads, K stored rotated.
+ * Decode runs steps 2-4 for one query per sequence; chunked prefill runs
+ * them for T consecutive rows of one sequence (leheavengame.com OCR 2
+ * release article, Sec. 3: the prefill scoring temporary of shape
+ * [tokens, context/32] is never materialised here).
+ *
+ * Conventions for every entry point:
+ *  - bf16 tensors are passed as uint16_t bit patterns.  Every pointer
+ *    argument, unless stated otherwise, is a DEVICE pointer, 16-byte aligned,
+ *    owned by the caller.  The library never allocates, frees or
+ *    synchronises; scratch memory comes from caller-provided workspaces whose
+ *    size uocr_workspace_size() returns.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *    asynchronous and ordered on that stream.
+ *  - Return value: UOCR_OK or an error code.  All argument checks run on the
+ *    host before any HIP call; a call that fails them launches nothing and
+ *    writes nothing.  uocr_last_error() gives a thread-local message.
+ *  - Values read on the device (ctx_lens, block tables, block ids) are not
+ *    visible to the host checks; kernels clamp a context length to
+ *    [0, 32*max_blocks] and skip any block id or pool index out of range, so
+ *    corrupt tables cannot make a kernel access memory out of bounds.
+ *  - Query at position p sees keys 0..p; its own K/V (and, in prefill, the
+ *    whole chunk's) must already be in the cache.
+ */
+#ifndef UOCR_SPARSE_H
+#define UOCR_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define UOCR_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+  UOCR_OK = 0,
+  UOCR_EINVAL = 1,      /* null pointer, misaligned pointer, bad config field  */
+  UOCR_ESHAPE = 2,      /* sizes or offsets out of the supported range          */
+  UOCR_EWORKSPACE = 3,  /* workspace missing or smaller than required           */
+  UOCR_EHIP = 4,        /* a HIP launch reported an error                       */
+  UOCR_EUNSUPPORTED = 5 /* valid but not supported by this build (see fields)   */
+};
+
+/* Operation ids for uocr_workspace_size(). */
+enum {
+  UOCR_OP_INDEXER_DECODE = 0,
+  UOCR_OP_TOPK_DECODE = 1,
+  UOCR_OP_ATTN_DECODE = 2,
+  UOCR_OP_INDEXER_PREFILL = 3,
+  UOCR_OP_TOPK_PREFILL = 4,
+  UOCR_OP_ATTN_PREFILL = 5
+};
+
+/*
+ * Sparse-attention configuration; the field names follow the released
+ * model's sparse_attention_config (news.rkmt.cn/news/25027 Sec. 5 step 3).
+ */
+typedef struct uocr_sparse_cfg {
+  int32_t block_size;   /* sparse_block_size: tokens per block; must be 32              */
+  int32_t topk_blocks;  /* sparse_topk_blocks: kept blocks per query, local included
+                           (16); local_blocks <= topk_blocks <= 4096                    */
+  int32_t local_blocks; /* sparse_local_block: most recent blocks always kept (4);
+                           >= 1                                                         */
+  int32_t num_heads;    /* attention heads H (10), K/V heads equal; 1..64               */
+  int32_t head_dim;     /* D; must be 128                                               */
+  int32_t index_dim;    /* indexer dim Di; must be 128                                  */
+  float sm_scale;       /* softmax scale applied to q.k (1/sqrt(128)); finite, > 0      */
+} uocr_sparse_cfg;
+
+/*
+ * One layer's KV cache, block-major.  Pool block b holds 32 consecutive
+ * tokens of one sequence:
+ *   k_pool, v_pool : [num_blocks][H][32][D] bf16, K already rotated
+ *   kidx_pool      : [num_blocks][32][Di]  bf16 (indexer keys)
+ *   block_table    : [batch][max_blocks] int32, pool block of each logical
+ *                    block of each sequence (entries past a sequence's end are
+ *                    ignored)
+ *   ctx_lens       : [batch] int32, tokens in the cache per sequence
+ * A block x head of K or V is one contiguous 8 KB row group, an indexer block
+ * one contiguous 8 KB tile, so every gather is fully coalesced.
+ */
+typedef struct uocr_kv {
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const uint16_t* kidx_pool;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  int64_t num_blocks;  /* pool blocks P (>= 1)                               */
+  int32_t batch;       /* sequences B (>= 0)                                 */
+  int32_t max_blocks;  /* block-table row length (>= 1, <= 1,048,576)        */
+} uocr_kv;
+
+/* ---------------------------------------------------------------- decode */
+
+/*
+ * Steps 2 (scoring + block max) for one decode query per sequence
+ * (news.rkmt.cn/news/25027 Sec. 5 step 2).
+ *   q_idx        : [batch][Di] bf16 indexer query of each sequence
+ *   block_scores : [batch][max_blocks] float32, written.  For sequence b with
+ *                  p = ctx_len-1 and nb = p/32+1 blocks, entry j < nb-local
+ *                  (a remote candidate) is max over the block's 32 keys of
+ *                  q_idx . kidx (float32 accumulation of exact bf16 products);
+ *                  every other entry is -inf.
+ * Uses the k_pool/v_pool fields of kv only for validation (may be NULL).
+ */
+int uocr_indexer_score_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q_idx,
+                              float* block_scores, void* stream);
+
+/*
+ * Step 3 for one decode query per sequence (news.rkmt.cn/news/25027 Sec. 5
+ * step 3): keeps blocks nb-local..nb-1 and the (topk-local) highest-scoring
+ * candidates 0..nb-local-1, ranked by score descending with the lower block id
+ * first on ties (-0.0 equals +0.0, NaN ranks last); all candidates when there
+ * are no more of them than remote slots.
+ *   block_scores : [batch][max_blocks] float32 (as written above)
+ *   ctx_lens     : [batch] int32
+ *   block_idx    : [batch][topk_blocks] int32, written: kept block ids
+ *                  ascending, then -1 padding
+ *   n_sel        : [batch] int32 or NULL, written: min(topk, nb)
+ */
+int uocr_block_topk_decode(const uocr_sparse_cfg* cfg, const float* block_scores, const int32_t* ctx_lens,
+                           int32_t batch, int32_t max_blocks, int32_t* block_idx, int32_t* n_sel,
+                           void* stream);
+
+/*
+ * Step 4 for one decode query per sequence (news.rkmt.cn/news/25027 Sec. 5
+ * step 4): per head h, softmax over the kept tokens (blocks in block_idx,
+ * tokens <= p) of sm_scale * q_h . k_h, times V.
+ *   q         : [batch][H][D] bf16
+ *   block_idx : [batch][topk_blocks] int32, distinct block ids in any order;
+ *               entries < 0 or >= max_blocks are skipped
+ *   out       : [batch][H][D] float32, written (0 when no token is kept)
+ *   lse       : [batch][H] float32 or NULL, natural-log log-sum-exp of the
+ *               scaled logits (-inf when no token is kept)
+ *   ws        : workspace of uocr_workspace_size(cfg, UOCR_OP_ATTN_DECODE,
+ *               batch, max_blocks) bytes (NULL allowed when that is 0)
+ */
+int uocr_sparse_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q,
+                            const int32_t* block_idx, float* out, float* lse, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------- chunked prefill */
+
+/*
+ * Step 2 for rows t = 0..T-1 of a prefill chunk of sequence 0 of kv
+ * (kv->batch must be 1), row t at position p = q_start + t
+ * (leheavengame.com OCR 2 release article, Sec. 3, chunked prefill;
+ * news.rkmt.cn/news/25027 Sec. 5 step 2).  The dense [T x keys] indexer
+ * product runs on bf16 MFMA; scores are max-reduced per block in registers
+ * and only each row's best (topk-local) candidates per context split are
+ * written to cand_ws (an opaque workspace consumed by
+ * uocr_block_topk_prefill), never the [T, context/32] score matrix.
+ *   q_idx   : [T][Di] bf16
+ *   cand_ws : workspace of uocr_workspace_size(cfg, UOCR_OP_INDEXER_PREFILL,
+ *             T, max_blocks) bytes
+ * Requires 0 <= q_start, T >= 0, q_start + T <= 32 * max_blocks,
+ * topk_blocks - local_blocks <= 16.
+ */
+int uocr_indexer_score_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q_idx,
+                               int32_t q_start, int32_t T, void* cand_ws, size_t cand_ws_bytes, void* stream);
+
+/*
+ * Step 3 for the rows scored by uocr_indexer_score_prefill with the same
+ * cfg, q_start, T and max_blocks: merges each row's per-split candidates
+ * under the decode ranking rule and adds the row's local blocks.
+ *   block_idx : [T][topk_blocks] int32, written (ascending, -1 padded)
+ *   n_sel     : [T] int32 or NULL
+ */
+int uocr_block_topk_prefill(const uocr_sparse_cfg* cfg, const void* cand_ws, size_t cand_ws_bytes,
+                            int32_t q_start, int32_t T, int32_t max_blocks, int32_t* block_idx,
+                            int32_t* n_sel, void* stream);
+
+/*
+ * Step 4 for prefill rows: as uocr_sparse_attn_decode with one query per row
+ * at p = q_start + t, all rows in sequence 0 of kv (kv->batch must be 1).
+ *   q   : [T][H][D] bf16;  block_idx : [T][topk_blocks] int32
+ *   out : [T][H][D] float32;  lse : [T][H] float32 or NULL
+ */
+int uocr_sparse_attn_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q, int32_t q_start,
+                             int32_t T, const int32_t* block_idx, float* out, float* lse, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------- utilities */
+
+/*
+ * Bytes of workspace operation `op` needs for `rows` queries (decode: batch;
+ * prefill: T) and a block-table row length `max_blocks`; 0 when the
+ * operation needs none or the arguments are invalid.
+ */
+size_t uocr_workspace_size(const uocr_sparse_cfg* cfg, int32_t op, int32_t rows, int32_t max_blocks);
+
+/* Static text of a status code. */
+const char* uocr_status_string(int32_t status);
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char* uocr_last_error(void);
+
+/* UOCR_ABI_VERSION of the built library. */
+int32_t uocr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UOCR_SPARSE_H */

@@ -41,5 +41,7 @@ from .sr_swa import (  # noqa: F401
     attended_tokens,
     attend,
     decode_query,
+    decode_query_fetch,
     prefill_rows,
+    prefill_rows_fetch,
 )

@@ -193,17 +193,31 @@ def decode_query(q_bits, q_idx_bits, k_bits, v_bits, kidx_bits, ctx_len: int,
     p = ctx_len - 1.  k_bits/v_bits: [H, >=ctx_len, D]; kidx_bits:
     [>=ctx_len, Di]; q_bits [H, D]; q_idx_bits [Di].
     """
+    return decode_query_fetch(q_bits, q_idx_bits, kidx_bits,
+                              lambda toks: (k_bits[:, toks, :], v_bits[:, toks, :]), ctx_len, cfg)
+
+
+def decode_query_fetch(q_bits, q_idx_bits, kidx_bits, fetch_kv, ctx_len: int,
+                       cfg: SparseCfg = SparseCfg()):
+    """``decode_query`` with K/V supplied on demand.
+
+    ``fetch_kv(tokens)`` returns (K, V) bf16 bits [H, len(tokens), D] of the
+    given token positions; only the attended tokens are ever requested, so
+    callers need not materialise a whole 128K-token cache.
+    """
+    H, D = np.asarray(q_bits).shape
     if ctx_len <= 0:
-        H, D = np.asarray(q_bits).shape
-        return {"selected": [], "out": np.zeros((H, D)), "lse": np.full(H, -np.inf),
-                "block_scores": np.zeros(0, np.float32), "cutoff": None, "tokens": np.zeros(0, np.int64)}
+        return {"selected": [], "remote": [], "local": [], "out": np.zeros((H, D)), "lse": np.full(H, -np.inf),
+                "block_scores": np.zeros(0, np.float32), "cutoff": None, "ranked": np.zeros(0, np.int64),
+                "tokens": np.zeros(0, np.int64)}
     p = ctx_len - 1
     ncand = candidate_count(p, cfg)
     scores = indexer_scores(q_idx_bits, kidx_bits[: ncand * cfg.block_size])
     bscores = block_maxima(scores, p, ncand, cfg)
     sel = select_blocks(bscores, p, cfg)
     toks = attended_tokens(sel["selected"], p, cfg)
-    out, lse = attend(q_bits, k_bits, v_bits, toks, cfg.sm_scale)
+    k_rows, v_rows = fetch_kv(toks)
+    out, lse = attend(q_bits, k_rows, v_rows, np.arange(toks.size), cfg.sm_scale)
     sel.update(out=out, lse=lse, tokens=toks)
     return sel
 
@@ -217,10 +231,16 @@ def prefill_rows(q_bits, q_idx_bits, k_bits, v_bits, kidx_bits, q_start: int,
     chunked prefill; the per-row rule is the decode rule at that position).
     q_bits [T, H, D], q_idx_bits [T, Di].  Returns one dict per row.
     """
+    return prefill_rows_fetch(q_bits, q_idx_bits, kidx_bits,
+                              lambda toks: (k_bits[:, toks, :], v_bits[:, toks, :]), q_start, rows, cfg)
+
+
+def prefill_rows_fetch(q_bits, q_idx_bits, kidx_bits, fetch_kv, q_start: int,
+                       rows: Sequence[int], cfg: SparseCfg = SparseCfg()):
+    """``prefill_rows`` with K/V supplied on demand (see decode_query_fetch)."""
     res = []
     for t in rows:
-        r = decode_query(q_bits[t], q_idx_bits[t], k_bits, v_bits, kidx_bits,
-                         q_start + t + 1, cfg)
+        r = decode_query_fetch(q_bits[t], q_idx_bits[t], kidx_bits, fetch_kv, q_start + t + 1, cfg)
         r["row"] = t
         res.append(r)
     return res

@@ -131,6 +131,14 @@ class Workload:
         v = self._values(self.key(role, layer, seq), idx.ravel()).reshape(t1 - t0, H, D)
         return np.ascontiguousarray(v.transpose(1, 0, 2))
 
+    def kv_tokens(self, role: int, layer: int, seq: int, toks: np.ndarray) -> np.ndarray:
+        """Main K or V of arbitrary token positions: [H, len(toks), D]."""
+        H, D = self.heads, self.head_dim
+        t = np.asarray(toks, dtype=np.int64)
+        idx = ((t[:, None, None] * H + np.arange(H)[None, :, None]) * D + np.arange(D)[None, None, :])
+        v = self._values(self.key(role, layer, seq), idx.ravel()).reshape(t.size, H, D)
+        return np.ascontiguousarray(v.transpose(1, 0, 2))
+
     def kidx(self, layer: int, seq: int, t0: int, t1: int) -> np.ndarray:
         """Indexer keys of tokens [t0, t1), edits applied: [t1-t0, Di]."""
         Di = self.index_dim

@@ -1,0 +1,178 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/uocr_sparse.h declares, and rejects bad arguments on the
+host before any HIP call."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uocr_sparse.h")
+
+
+def _ensure_built():
+    from block_sparse_long_sr_amd import build as B
+    lib = os.path.join(ROOT, "block_sparse_long_sr_amd", "libuocr_sparse.so")
+    if not os.path.exists(lib):
+        B.build()
+    return lib
+
+
+@pytest.fixture(scope="module")
+def U():
+    _ensure_built()
+    import block_sparse_long_sr_amd as U
+    return U
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(uocr_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["uocr_indexer_score_decode", "uocr_block_topk_decode", "uocr_sparse_attn_decode",
+              "uocr_indexer_score_prefill", "uocr_block_topk_prefill", "uocr_sparse_attn_prefill",
+              "uocr_workspace_size", "uocr_status_string", "uocr_last_error", "uocr_abi_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_ensure_built())
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_struct_layouts_match_header(U):
+    assert ctypes.sizeof(U.SparseCfg) == 28
+    assert ctypes.sizeof(U.KV) == 5 * 8 + 8 + 4 + 4
+    assert U.abi_version() == 1
+
+
+def test_status_strings(U):
+    assert U.status_string(0) == "UOCR_OK"
+    for c in range(1, 6):
+        assert U.status_string(c).startswith("UOCR_E")
+
+
+FAKE = 0x10000  # a 16-byte aligned fake device address; never dereferenced
+
+
+def _kv(U, batch=2, max_blocks=8, **kw):
+    d = dict(k_pool=FAKE, v_pool=FAKE, kidx_pool=FAKE, block_table=FAKE, ctx_lens=FAKE,
+             num_blocks=16, batch=batch, max_blocks=max_blocks)
+    d.update(kw)
+    return U.make_kv(d["k_pool"], d["v_pool"], d["kidx_pool"], d["block_table"], d["ctx_lens"],
+                     d["num_blocks"], d["batch"], d["max_blocks"])
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("block_size", 16, 1), ("head_dim", 64, 1), ("index_dim", 64, 1), ("local_blocks", 0, 1),
+    ("topk_blocks", 3, 1), ("topk_blocks", 5000, 1), ("num_heads", 0, 1), ("num_heads", 65, 1),
+    ("sm_scale", 0.0, 1), ("sm_scale", float("nan"), 1), ("sm_scale", float("inf"), 1),
+])
+def test_bad_config_rejected(U, field, value, code):
+    cfg = U.make_cfg()
+    setattr(cfg, field, value)
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_decode(cfg, _kv(U), FAKE, FAKE, stream=0)
+    assert e.value.status == code
+    assert field.split("_")[0] in U.last_error() or "must" in U.last_error()
+
+
+def test_decode_argument_checks(U):
+    cfg = U.make_cfg()
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_decode(cfg, _kv(U), None, FAKE, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_decode(cfg, _kv(U), FAKE + 8, FAKE, stream=0)   # misaligned bf16 pointer
+    assert e.value.status == 1 and "aligned" in U.last_error()
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_decode(cfg, _kv(U, max_blocks=0), FAKE, FAKE, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_decode(cfg, _kv(U, batch=70000), FAKE, FAKE, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_decode(cfg, _kv(U, num_blocks=0), FAKE, FAKE, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(U.UocrError) as e:
+        U.sparse_attn_decode(cfg, _kv(U, v_pool=None), FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == 1 and "v_pool" in U.last_error()
+    with pytest.raises(U.UocrError) as e:
+        U.block_topk_decode(cfg, FAKE, FAKE, 2, 8, None, stream=0)
+    assert e.value.status == 1 and "block_idx" in U.last_error()
+    with pytest.raises(U.UocrError) as e:
+        U.block_topk_decode(cfg, FAKE, FAKE, -1, 8, FAKE, stream=0)
+    assert e.value.status == 2
+
+
+def test_empty_batch_is_a_no_op(U):
+    cfg = U.make_cfg()
+    # batch 0: nothing to do, nothing launched, success without touching HIP
+    U.indexer_score_decode(cfg, _kv(U, batch=0), None, None, stream=0)
+    U.block_topk_decode(cfg, None, None, 0, 8, None, stream=0)
+    U.sparse_attn_decode(cfg, _kv(U, batch=0), None, None, None, stream=0)
+
+
+def test_prefill_argument_checks(U):
+    cfg = U.make_cfg()
+    kv1 = _kv(U, batch=1, max_blocks=64)
+    need = U.workspace_size(cfg, U.OP_INDEXER_PREFILL, 100, 64)
+    assert need > 0
+    assert need == U.workspace_size(cfg, U.OP_TOPK_PREFILL, 100, 64)
+    assert U.workspace_size(cfg, U.OP_ATTN_PREFILL, 100, 64) == 0
+    assert U.workspace_size(cfg, U.OP_ATTN_DECODE, 16, 4096) == 0
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_prefill(cfg, _kv(U, batch=2, max_blocks=64), FAKE, 0, 100, (FAKE, need), stream=0)
+    assert e.value.status == 2
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_prefill(cfg, kv1, FAKE, 2000, 100, (FAKE, need), stream=0)   # 2100 > 64*32
+    assert e.value.status == 2
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_prefill(cfg, kv1, FAKE, -1, 100, (FAKE, need), stream=0)
+    assert e.value.status == 2
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_prefill(cfg, kv1, FAKE, 0, 100, (FAKE, need - 1), stream=0)
+    assert e.value.status == 3
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_prefill(cfg, kv1, FAKE, 0, 100, None, stream=0)
+    assert e.value.status == 3
+    with pytest.raises(U.UocrError) as e:
+        U.block_topk_prefill(cfg, (FAKE, need - 1), 0, 100, 64, FAKE, stream=0)
+    assert e.value.status == 3
+    big = U.make_cfg(topk_blocks=40)
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_prefill(big, kv1, FAKE, 0, 100, (FAKE, 1 << 30), stream=0)
+    assert e.value.status == 5
+    with pytest.raises(U.UocrError) as e:
+        U.sparse_attn_prefill(cfg, kv1, FAKE, 2000, 100, FAKE, FAKE, stream=0)
+    assert e.value.status == 2
+    # T == 0 is a successful no-op
+    U.indexer_score_prefill(cfg, kv1, None, 0, 0, None, stream=0)
+    U.block_topk_prefill(cfg, None, 0, 0, 64, None, stream=0)
+    U.sparse_attn_prefill(cfg, kv1, None, 0, 0, None, None, stream=0)
+
+
+def test_last_error_is_cleared_by_success(U):
+    cfg = U.make_cfg()
+    with pytest.raises(U.UocrError):
+        U.block_topk_decode(cfg, FAKE, FAKE, -1, 8, FAKE, stream=0)
+    assert U.last_error() != ""
+    U.block_topk_decode(cfg, None, None, 0, 8, None, stream=0)
+    assert U.last_error() == ""
+
+
+def test_binding_rejects_non_contiguous_tensors(U):
+    import torch
+    cfg = U.make_cfg()
+    scores = torch.zeros(8, 4).t()          # a transposed view: not row-major
+    assert not scores.is_contiguous()
+    with pytest.raises(ValueError):
+        U.block_topk_decode(cfg, scores, FAKE, 4, 8, FAKE, stream=0)
