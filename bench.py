@@ -1,0 +1,316 @@
+"""Benchmark of the SR-SWA block-sparse attention hot path on one MI355X.
+
+Workload (the headline case): decode batch of 16 sequences x 12 layers at
+S = 131072 tokens (4096 blocks of 32), 10 heads x 128 bf16 K/V, 1 x 128
+indexer, 12 planted blocks per query, all resident in HBM (~135 GB).  One
+step = for each of the 12 layers, in order: indexer score + block max, top-k
+block selection, sparse attention -- the three decode entry points of the C
+ABI, 36 stream-ordered launches.  ``value`` is decode query-heads/s
+(16 * 12 * 10 per step).
+
+The same JSON line carries the roofline of the dominant kernel (the decode
+indexer, HBM bound) timed with HIP events, the CPU oracle's throughput on a
+bounded sample of the same workload, and the chunked-prefill case
+(2048 rows at offset 129024 of a 131072-token context) with the MFMA
+roofline of its scoring kernel.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn decode query-heads/s at 128K ctx; achieved HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = {
+    "indexer_decode": ["block_sparse_long_sr_amd/csrc/indexer_decode.hip",
+                       "block_sparse_long_sr_amd/csrc/device_common.h"],
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(wl, cfg_topk=16, local=4, heads=10, D=128, Di=128):
+    """Algorithmic HBM bytes of one decode layer launch triple, per kernel."""
+    idx_b = topk_b = attn_b = 0
+    for b in range(wl.batch):
+        L = int(wl.ctx_lens[b])
+        nb = -(-L // 32)
+        ncand = max(0, nb - local)
+        # indexer: candidate key tiles + their table entries + q_idx + ctx + score row written
+        idx_b += ncand * 32 * Di * 2 + ncand * 4 + Di * 2 + 4 + wl.max_blocks * 4
+        # top-k: candidate scores read + ctx + ids written
+        topk_b += ncand * 4 + 4 + cfg_topk * 4
+        # attention: K and V of the attended tokens + q + ids + table + out + lse
+        p = L - 1
+        toks = 15 * 32 + (p % 32) + 1 if nb >= 16 else L
+        attn_b += 2 * toks * heads * D * 2 + heads * D * 2 + cfg_topk * 4 * 2 + heads * D * 4 + heads * 4 + 4
+    return idx_b, topk_b, attn_b
+
+
+def traffic_for(kernel, per_launch_alg):
+    """Measured HBM bytes per launch from the committed rocprofv3 counter
+    summary, when it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(dev, wl, n_layers):
+    """Time the CPU oracle on (16 sequences x n_layers) decode queries of the
+    same workload.  Inputs are copied from device memory beforehand; the time
+    spent gathering K/V rows for the oracle is excluded."""
+    import numpy as np
+    import torch
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    tab = dev.block_table
+    B, L = wl.batch, wl.ctx_lens
+    total = 0.0
+    nq = 0
+    with threadpool_limits(limits=1):
+        for l in range(n_layers):
+            for b in range(B):
+                S = int(L[b])
+                nb = -(-S // 32)
+                blocks = tab[b, :nb].long()
+                ki = dev.kidx[l].index_select(0, blocks).reshape(nb * 32, -1)[:S]
+                ki = ki.cpu().numpy().view(np.uint16)
+                q = dev.q[l, b].cpu().numpy().view(np.uint16)
+                qi = dev.q_idx[l, b].cpu().numpy().view(np.uint16)
+                fetch_time = [0.0]
+
+                def fetch(toks, l=l, b=b):
+                    t0 = time.perf_counter()
+                    pb = tab[b, torch.from_numpy(toks // 32).to(tab.device)].long()
+                    off = torch.from_numpy(toks % 32).to(tab.device)
+                    k = dev.k[l].index_select(0, pb)[torch.arange(len(toks), device=tab.device), :, off, :]
+                    v = dev.v[l].index_select(0, pb)[torch.arange(len(toks), device=tab.device), :, off, :]
+                    r = (k.transpose(0, 1).contiguous().cpu().numpy().view(np.uint16),
+                         v.transpose(0, 1).contiguous().cpu().numpy().view(np.uint16))
+                    fetch_time[0] += time.perf_counter() - t0
+                    return r
+
+                t0 = time.perf_counter()
+                oracle.decode_query_fetch(q, qi, ki, fetch, S)
+                total += time.perf_counter() - t0 - fetch_time[0]
+                nq += 1
+    return nq, total
+
+
+def run_prefill(U, SD, W, torch, iters=5):
+    wl = W.config5()
+    dev = SD.generate(wl)
+    cfg = U.make_cfg()
+    T, M = wl.rows, wl.max_blocks
+    kv = dev.kv(0)
+    ws_bytes = U.workspace_size(cfg, U.OP_INDEXER_PREFILL, T, M)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    wsarg = (ws.data_ptr(), ws_bytes)
+    idx = torch.empty((T, 16), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, 10, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, 10), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters + 2)]
+    for i in range(iters + 2):
+        e = ev[i]
+        e[0].record(stream)
+        U.indexer_score_prefill(cfg, kv, dev.q_idx, wl.q_start, T, wsarg, stream=sh)
+        e[1].record(stream)
+        U.block_topk_prefill(cfg, wsarg, wl.q_start, T, M, idx, stream=sh)
+        e[2].record(stream)
+        U.sparse_attn_prefill(cfg, kv, dev.q, wl.q_start, T, idx, out, lse, stream=sh)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t_sc = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(2, iters + 2)) / iters
+    t_mg = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(2, iters + 2)) / iters
+    t_at = sum(ev[i][2].elapsed_time(ev[i][3]) for i in range(2, iters + 2)) / iters
+    # algorithmic work of the scoring kernel: every candidate (row, block) pair
+    rowblocks = sum(max(0, (wl.q_start + t) // 32 + 1 - 4) for t in range(T))
+    flops = rowblocks * 32 * 128 * 2
+    tflops = flops / (t_sc * 1e-3) / 1e12
+    attn_unique = int(wl.ctx_lens[0]) * 10 * 128 * 2 * 2
+    res = {
+        "workload": wl.name,
+        "rows": T,
+        "tokens_per_s": T / ((t_sc + t_mg + t_at) * 1e-3),
+        "ms": {"scoring": t_sc, "merge": t_mg, "attention": t_at},
+        "scoring_roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS,
+                             "flops_per_launch": flops, "traffic": None},
+        "attention_gathered_GBps": T * 2 * 512 * 10 * 128 * 2 / (t_at * 1e-3) / 1e9,
+        "attention_unique_bytes_upper": attn_unique,
+    }
+    del dev, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-layers", type=int, default=12,
+                    help="layers of the workload the CPU oracle is timed on (x16 queries)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the decode step shards by sequence with no communication, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_long_sr_amd as U
+    from synth import device as SD
+    from synth import workloads as W
+
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    wl = W.config3()
+    log(f"generating {wl.name} on the GPU")
+    dev = SD.generate(wl)
+    torch.cuda.synchronize()
+    pool_gb = (dev.k.numel() + dev.v.numel() + dev.kidx.numel()) * 2 / 1e9
+    log(f"generated in {time.time() - t0:.1f}s; pools {pool_gb:.1f} GB")
+
+    cfg = U.make_cfg()
+    B, M, L, H = wl.batch, wl.max_blocks, wl.layers, 10
+    scores = torch.empty((L, B, M), dtype=torch.float32, device="cuda")
+    idx = torch.empty((L, B, 16), dtype=torch.int32, device="cuda")
+    out = torch.empty((L, B, H, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((L, B, H), dtype=torch.float32, device="cuda")
+    kvs = [dev.kv(l) for l in range(L)]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def layer(l):
+        U.indexer_score_decode(cfg, kvs[l], dev.q_idx[l], scores[l], stream=sh)
+        U.block_topk_decode(cfg, scores[l], dev.ctx_lens, B, M, idx[l], stream=sh)
+        U.sparse_attn_decode(cfg, kvs[l], dev.q[l], idx[l], out[l], lse[l], stream=sh)
+
+    def step():
+        for l in range(L):
+            layer(l)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    qh_per_s = B * L * H * args.steps / (ms_total * 1e-3)
+    log(f"decode step {ms_step * 1e3:.1f} us, {qh_per_s / 1e6:.3f} M query-heads/s")
+
+    # Per-kernel durations with events bracketing each launch (separate pass).
+    ksteps = max(3, min(10, args.steps))
+    evs = []
+    for _ in range(ksteps):
+        for l in range(L):
+            a, b_, c, d = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+            a.record(stream)
+            U.indexer_score_decode(cfg, kvs[l], dev.q_idx[l], scores[l], stream=sh)
+            b_.record(stream)
+            U.block_topk_decode(cfg, scores[l], dev.ctx_lens, B, M, idx[l], stream=sh)
+            c.record(stream)
+            U.sparse_attn_decode(cfg, kvs[l], dev.q[l], idx[l], out[l], lse[l], stream=sh)
+            d.record(stream)
+            evs.append((a, b_, c, d))
+    torch.cuda.synchronize()
+    n = len(evs)
+    t_idx = sum(a.elapsed_time(b_) for a, b_, _, _ in evs) / n
+    t_topk = sum(b_.elapsed_time(c) for _, b_, c, _ in evs) / n
+    t_attn = sum(c.elapsed_time(d) for _, _, c, d in evs) / n
+    idx_bytes, topk_bytes, attn_bytes = decode_bytes(wl)
+    achieved = idx_bytes / (t_idx * 1e-3) / 1e9
+    step_bytes = L * (idx_bytes + topk_bytes + attn_bytes)
+    log(f"indexer {t_idx * 1e3:.1f} us ({achieved:.0f} GB/s), topk {t_topk * 1e3:.1f} us, "
+        f"attention {t_attn * 1e3:.1f} us")
+
+    result = {
+        "metric": METRIC,
+        "value": qh_per_s,
+        "unit": "query-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "layers": L, "ctx_len": int(wl.ctx_lens[0]),
+                   "heads": H, "head_dim": 128, "block_size": 32, "topk_blocks": 16, "local_blocks": 4,
+                   "queries_per_step": B * L, "plant": wl.notes},
+        "tokens_per_s": B / (ms_step * 1e-3),
+        "step_hbm_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "step_algorithmic_bytes": step_bytes,
+        "kernel_us": {"indexer_score_decode": t_idx * 1e3, "block_topk_decode": t_topk * 1e3,
+                      "sparse_attn_decode": t_attn * 1e3},
+        "roofline": {"kernel": "indexer_score_decode", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "algorithmic_bytes_per_launch": idx_bytes,
+                     "traffic": traffic_for("indexer_decode", idx_bytes)},
+    }
+
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {16 * args.cpu_layers} query-layers")
+        nq, secs = cpu_baseline(dev, wl, args.cpu_layers)
+        result["cpu_baseline"] = {
+            "value": nq * H / secs, "unit": "query-heads/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nq} decode query-layers ({args.cpu_layers} layers x 16 sequences) of the same "
+                      f"workload, oracle time only (inputs copied from device memory beforehand), "
+                      f"{secs:.1f} s on 1 thread",
+        }
+        log(f"cpu oracle {nq * H / secs:.1f} query-heads/s")
+
+    del dev, scores, out
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
+        log("chunked prefill T=2048 at 129024 of 131072")
+        result["prefill"] = run_prefill(U, SD, W, torch)
+        log(f"prefill scoring {result['prefill']['ms']['scoring'] * 1e3:.1f} us "
+            f"({result['prefill']['scoring_roofline']['achieved']:.0f} TFLOP/s)")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
