@@ -67,17 +67,26 @@ def decode_bytes(wl, cfg_topk=16, local=4, heads=10, D=128, Di=128):
     return idx_b, topk_b, attn_b
 
 
-def traffic_for(kernel, per_launch_alg):
-    """Measured HBM bytes per launch from the committed rocprofv3 counter
-    summary, when it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+TRAFFIC_FILES = {"indexer_decode": "profiles/indexer_score_decode_128k_traffic.txt"}
+
+
+def traffic_for(kernel):
+    """Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE,
+    copy-calibrated) from the committed summary, or None when the summary is
+    missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, TRAFFIC_FILES[kernel])
     if not os.path.exists(path):
         return None
+    rec = {}
     with open(path) as f:
-        rec = json.load(f)
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
     if rec.get("source_digest") != source_digest(KERNEL_SOURCES[kernel]):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return int(float(rec["hbm_bytes_per_launch"]))
 
 
 def cpu_baseline(dev, wl, n_layers):
@@ -181,6 +190,8 @@ def main():
                     help="layers of the workload the CPU oracle is timed on (x16 queries)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy 1 GiB device-to-device 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
@@ -189,6 +200,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        torch.cuda.set_device(0)
+        a = torch.ones(1 << 29, dtype=torch.int16, device="cuda")   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": a.numel() * 2, "copies": 5}))
+        return
 
     import block_sparse_long_sr_amd as U
     from synth import device as SD
@@ -287,7 +308,7 @@ def main():
         "roofline": {"kernel": "indexer_score_decode", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "algorithmic_bytes_per_launch": idx_bytes,
-                     "traffic": traffic_for("indexer_decode", idx_bytes)},
+                     "traffic": traffic_for("indexer_decode")},
     }
 
     if not args.no_cpu_baseline:

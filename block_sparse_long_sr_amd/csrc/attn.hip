@@ -4,8 +4,9 @@
 // chunked prefill share the kernel; a prefill row is a query of sequence 0
 // at p = q_start + row.
 //
-// One 512-thread workgroup per (query, head): the kept blocks are split over
-// its 8 waves (split-K), each wave keeps an online-softmax state (running
+// One 1024-thread workgroup per (query, head): the kept blocks are split over
+// its 16 waves (split-K; at 16 kept blocks every block's K and V loads are in
+// flight at once), each wave keeps an online-softmax state (running
 // max, sum, 128-dim accumulator) and the waves' states are merged through LDS
 // at the end.  A wave reads a block's 8 KB K tile and 8 KB V tile with
 // contiguous 1 KB loads: lane l holds dims 8*(l%16)..+8 of keys 4k + l/16
@@ -18,7 +19,7 @@
 namespace uocr {
 
 namespace {
-constexpr int kAttnThreads = 512;
+constexpr int kAttnThreads = 1024;
 constexpr int kAttnWaves = kAttnThreads / kWave;
 }  // namespace
 

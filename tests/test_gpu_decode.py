@@ -123,6 +123,39 @@ def test_topk_kernel_ties_nan_signed_zero():
         assert nsel[b].item() == min(16, p // 32 + 1)
 
 
+@pytest.mark.parametrize("M,topk,pattern", [
+    (4100, 16, "normal"),      # 256-thread register variant, full
+    (10000, 16, "normal"),     # 1024-thread register variant
+    (20000, 16, "normal"),     # generic variant (scores re-read per pass)
+    (2000, 16, "all_equal"),   # > 512 ties at the cutoff: ordered compaction
+    (3000, 600, "normal"),     # R > 512: ordered compaction
+    (3000, 600, "int"),        # R > 512 with ties
+    (20000, 40, "int"),        # generic variant with ties
+])
+def test_topk_kernel_variants_direct(M, topk, pattern):
+    cfg_u, cfg_o = U.make_cfg(topk_blocks=topk), G.ocfg(topk=topk)
+    rng = np.random.default_rng(M + topk)
+    B = 3
+    lens = np.array([M * 32, M * 32 - 40, (M // 2) * 32 + 7], np.int32)
+    if pattern == "normal":
+        sc = rng.standard_normal((B, M)).astype(np.float32)
+    elif pattern == "int":
+        sc = rng.integers(-4, 4, (B, M)).astype(np.float32)
+    else:
+        sc = np.full((B, M), 2.5, np.float32)
+    scores = torch.from_numpy(sc).cuda()
+    ctx = torch.from_numpy(lens).cuda()
+    idx = torch.full((B, topk), -9, dtype=torch.int32, device="cuda")
+    U.block_topk_decode(cfg_u, scores, ctx, B, M, idx)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    for b in range(B):
+        p = int(lens[b]) - 1
+        ref = oracle.select_blocks(sc[b, : oracle.candidate_count(p, cfg_o)], p, cfg_o)
+        got = [int(x) for x in idx[b] if x >= 0]
+        assert got == ref["selected"], (b, got[:20], ref["selected"][:20])
+
+
 def test_deterministic_and_order_free():
     wl = _wl("determinism", 0xE5, [20000, 5000])
     dev = SD.generate(wl)
