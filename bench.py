@@ -190,6 +190,8 @@ def main():
                     help="layers of the workload the CPU oracle is timed on (x16 queries)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the chunked-prefill case (profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device-to-device 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -216,6 +218,9 @@ def main():
     from synth import workloads as W
 
     torch.cuda.set_device(0)
+    if args.prefill_only:
+        print(json.dumps({"prefill": run_prefill(U, SD, W, torch)}), flush=True)
+        return
     t0 = time.time()
     wl = W.config3()
     log(f"generating {wl.name} on the GPU")

@@ -27,6 +27,9 @@ DEVICE_FLAGS = [
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC"]
 
 SOURCES = ["api.cpp", "indexer_decode.hip", "topk_decode.hip", "attn.hip", "indexer_prefill.hip"]
+# MFMA results in ordinary VGPRs: the prefill epilogue reads every accumulator
+# with vector ALU instructions, which AGPRs would first have to be copied out of.
+PER_FILE_FLAGS = {"indexer_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _run(cmd):
@@ -44,7 +47,7 @@ def compile_objects(sources, src_dir, obj_dir, extra=()):
         src = os.path.join(src_dir, s)
         obj = os.path.join(obj_dir, os.path.splitext(s)[0] + ".o")
         if s.endswith(".hip"):
-            cmd = [HIPCC, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
+            cmd = [HIPCC, *DEVICE_FLAGS, *PER_FILE_FLAGS.get(s, []), *extra, "-c", src, "-o", obj]
         else:
             cmd = [HIPCC, *HOST_FLAGS, *extra, "-c", src, "-o", obj]
         jobs.append((cmd, obj))

@@ -36,6 +36,7 @@ constexpr int32_t kMaxBatch = 65535;
 constexpr int32_t kMaxBlocks = 1 << 20;
 constexpr int32_t kMaxHeads = 64;
 constexpr int32_t kMaxRemotePrefill = 16;
+constexpr int32_t kMaxBlocksPrefill = 32768;  // 64 splits of <= 512 blocks (in-split index <= 9 bits)
 
 int check_cfg(const uocr_sparse_cfg* c) {
   if (c == nullptr) return fail(UOCR_EINVAL, "cfg is NULL");
@@ -106,6 +107,15 @@ int check_prefill_range(const uocr_kv* kv, int32_t q_start, int32_t T) {
   if ((int64_t)q_start + T > (int64_t)kv->max_blocks * 32)
     return fail(UOCR_ESHAPE, "q_start + T (%lld) exceeds 32 * max_blocks (%lld)", (long long)q_start + T,
                 (long long)kv->max_blocks * 32);
+  return UOCR_OK;
+}
+
+int check_prefill_selection(const uocr_sparse_cfg* cfg, int32_t max_blocks) {
+  if (cfg->topk_blocks - cfg->local_blocks > kMaxRemotePrefill)
+    return fail(UOCR_EUNSUPPORTED, "prefill supports topk_blocks - local_blocks <= %d (got %d)", kMaxRemotePrefill,
+                cfg->topk_blocks - cfg->local_blocks);
+  if (max_blocks > kMaxBlocksPrefill)
+    return fail(UOCR_EUNSUPPORTED, "prefill supports max_blocks <= %d (got %d)", kMaxBlocksPrefill, max_blocks);
   return UOCR_OK;
 }
 
@@ -200,9 +210,7 @@ int uocr_indexer_score_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, co
   TRY(check_cfg(cfg));
   TRY(check_kv(kv, true, false));
   TRY(check_prefill_range(kv, q_start, T));
-  if (cfg->topk_blocks - cfg->local_blocks > kMaxRemotePrefill)
-    return fail(UOCR_EUNSUPPORTED, "prefill supports topk_blocks - local_blocks <= %d (got %d)", kMaxRemotePrefill,
-                cfg->topk_blocks - cfg->local_blocks);
+  TRY(check_prefill_selection(cfg, kv->max_blocks));
   const uocr::PrefillPlan plan = uocr::prefill_plan(T, kv->max_blocks, cfg->topk_blocks, cfg->local_blocks);
   if (T == 0 || plan.R == 0) return ok();
   REQ_PTR16(q_idx, "q_idx");
@@ -214,8 +222,7 @@ int uocr_indexer_score_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, co
   a.kidx_pool = kv->kidx_pool;
   a.block_table = kv->block_table;
   a.q_idx = q_idx;
-  a.cand_keys = reinterpret_cast<uint32_t*>(static_cast<char*>(cand_ws) + uocr::prefill_keys_offset());
-  a.cand_idx = reinterpret_cast<int32_t*>(static_cast<char*>(cand_ws) + uocr::prefill_idx_offset(plan, T));
+  a.cand_keys = static_cast<uint32_t*>(cand_ws);
   a.num_blocks = kv->num_blocks;
   a.T = T;
   a.q_start = q_start;
@@ -233,8 +240,7 @@ int uocr_block_topk_prefill(const uocr_sparse_cfg* cfg, const void* cand_ws, siz
   if (T < 0) return fail(UOCR_ESHAPE, "T must be >= 0 (got %d)", T);
   if ((int64_t)q_start + T > (int64_t)max_blocks * 32)
     return fail(UOCR_ESHAPE, "q_start + T exceeds 32 * max_blocks");
-  if (cfg->topk_blocks - cfg->local_blocks > kMaxRemotePrefill)
-    return fail(UOCR_EUNSUPPORTED, "prefill supports topk_blocks - local_blocks <= %d", kMaxRemotePrefill);
+  TRY(check_prefill_selection(cfg, max_blocks));
   if (T == 0) return ok();
   REQ_PTR4(block_idx, "block_idx");
   OPT_PTR4(n_sel, "n_sel");
@@ -246,8 +252,7 @@ int uocr_block_topk_prefill(const uocr_sparse_cfg* cfg, const void* cand_ws, siz
       return fail(UOCR_EWORKSPACE, "cand_ws has %zu bytes, %zu needed", cand_ws_bytes, plan.ws_bytes);
   }
   uocr::TopkPrefillArgs a{};
-  a.cand_keys = reinterpret_cast<const uint32_t*>(static_cast<const char*>(cand_ws) + uocr::prefill_keys_offset());
-  a.cand_idx = reinterpret_cast<const int32_t*>(static_cast<const char*>(cand_ws) + uocr::prefill_idx_offset(plan, T));
+  a.cand_keys = static_cast<const uint32_t*>(cand_ws);
   a.block_idx = block_idx;
   a.n_sel = n_sel;
   a.T = T;
@@ -275,7 +280,7 @@ size_t uocr_workspace_size(const uocr_sparse_cfg* cfg, int32_t op, int32_t rows,
   switch (op) {
     case UOCR_OP_INDEXER_PREFILL:
     case UOCR_OP_TOPK_PREFILL:
-      if (cfg->topk_blocks - cfg->local_blocks > kMaxRemotePrefill) return 0;
+      if (cfg->topk_blocks - cfg->local_blocks > kMaxRemotePrefill || max_blocks > kMaxBlocksPrefill) return 0;
       return uocr::prefill_plan(rows, max_blocks, cfg->topk_blocks, cfg->local_blocks).ws_bytes;
     default:
       return 0;

@@ -62,6 +62,7 @@ struct PrefillPlan {
   int32_t bps;       // blocks per split
   int32_t nsplit;    // splits (<= 64)
   int32_t R;         // remote slots = topk - local
+  int32_t idbits;    // low key bits that carry the in-split block index
   size_t ws_bytes;   // candidate workspace size
 };
 PrefillPlan prefill_plan(int32_t T, int32_t max_blocks, int32_t topk, int32_t local_blocks);
@@ -70,8 +71,7 @@ struct IndexerPrefillArgs {
   const uint16_t* kidx_pool;
   const int32_t* block_table;  // row of sequence 0
   const uint16_t* q_idx;       // [T][128]
-  uint32_t* cand_keys;         // [T][nsplit][R]
-  int32_t* cand_idx;           // [T][nsplit][R]
+  uint32_t* cand_keys;         // [T][nsplit][R] packed keys, 0 = empty
   int64_t num_blocks;
   int32_t T;
   int32_t q_start;
@@ -83,7 +83,6 @@ hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t strea
 
 struct TopkPrefillArgs {
   const uint32_t* cand_keys;
-  const int32_t* cand_idx;
   int32_t* block_idx;  // [T][topk]
   int32_t* n_sel;
   int32_t T;
@@ -94,11 +93,8 @@ struct TopkPrefillArgs {
 };
 hipError_t launch_topk_prefill(const TopkPrefillArgs& a, hipStream_t stream);
 
-// Layout of the opaque prefill candidate workspace.
-inline size_t prefill_keys_offset() { return 0; }
-inline size_t prefill_idx_offset(const PrefillPlan& p, int32_t T) {
-  size_t n = (size_t)T * (size_t)p.nsplit * (size_t)p.R * sizeof(uint32_t);
-  return (n + 255) & ~(size_t)255;
-}
+// Largest in-split index width: packed prefill keys keep 32 - idbits order
+// bits, i.e. scores are ranked to 2^-(23 - idbits) relative.
+constexpr int32_t kMaxIdBits = 9;
 
 }  // namespace uocr
