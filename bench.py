@@ -186,6 +186,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--separate", action="store_true",
+                    help="run selection and attention as two launches instead of the fused one")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="micro-batches of sequences, each on its own HIP stream (default priority)")
     ap.add_argument("--cpu-layers", type=int, default=12,
                     help="layers of the workload the CPU oracle is timed on (x16 queries)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -239,23 +243,62 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    def layer(l):
-        U.indexer_score_decode(cfg, kvs[l], dev.q_idx[l], scores[l], stream=sh)
-        U.block_topk_decode(cfg, scores[l], dev.ctx_lens, B, M, idx[l], stream=sh)
-        U.sparse_attn_decode(cfg, kvs[l], dev.q[l], idx[l], out[l], lse[l], stream=sh)
+    # Micro-batches: the sequences are independent, so the batch is split into
+    # `streams` groups, each running its 12 layers in order on its own stream;
+    # one group's latency-bound selection/attention overlaps another group's
+    # bandwidth-bound scoring.  Each group uses the same entry points on views
+    # of the batch (descriptor pointers offset by the group's first sequence).
+    ns = max(1, min(args.streams, B))
+    bounds = [(B * i) // ns for i in range(ns + 1)]
+    groups = []
+    for i in range(ns):
+        b0, b1 = bounds[i], bounds[i + 1]
+        gkv = []
+        for l in range(L):
+            gkv.append(U.make_kv(dev.k[l], dev.v[l], dev.kidx[l], dev.block_table[b0:b1], dev.ctx_lens[b0:b1],
+                                 wl.pool_blocks, b1 - b0, M))
+        groups.append((b0, b1, gkv, torch.cuda.Stream() if ns > 1 else stream))
 
     def step():
         for l in range(L):
-            layer(l)
+            for b0, b1, gkv, st in groups:
+                h_ = st.cuda_stream
+                U.indexer_score_decode(cfg, gkv[l], dev.q_idx[l, b0:b1], scores[l, b0:b1], stream=h_)
+                if args.separate:
+                    U.block_topk_decode(cfg, scores[l, b0:b1], dev.ctx_lens[b0:b1], b1 - b0, M, idx[l, b0:b1],
+                                        stream=h_)
+                    U.sparse_attn_decode(cfg, gkv[l], dev.q[l, b0:b1], idx[l, b0:b1], out[l, b0:b1],
+                                         lse[l, b0:b1], stream=h_)
+                else:
+                    U.topk_attn_decode(cfg, gkv[l], dev.q[l, b0:b1], scores[l, b0:b1], idx[l, b0:b1],
+                                       out[l, b0:b1], lse[l, b0:b1], stream=h_)
 
+    def fork():
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        for _, _, _, st in groups:
+            if st is not stream:
+                st.wait_event(ev)
+
+    def join():
+        for _, _, _, st in groups:
+            if st is not stream:
+                ev = torch.cuda.Event()
+                ev.record(st)
+                stream.wait_event(ev)
+
+    fork()
     for _ in range(args.warmup):
         step()
+    join()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
+    fork()
     for _ in range(args.steps):
         step()
+    join()
     e1.record(stream)
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
@@ -282,11 +325,21 @@ def main():
     t_idx = sum(a.elapsed_time(b_) for a, b_, _, _ in evs) / n
     t_topk = sum(b_.elapsed_time(c) for _, b_, c, _ in evs) / n
     t_attn = sum(c.elapsed_time(d) for _, _, c, d in evs) / n
+    fev = []
+    for _ in range(ksteps):
+        for l in range(L):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            U.topk_attn_decode(cfg, kvs[l], dev.q[l], scores[l], idx[l], out[l], lse[l], stream=sh)
+            b_.record(stream)
+            fev.append((a_, b_))
+    torch.cuda.synchronize()
+    t_fused = sum(a_.elapsed_time(b_) for a_, b_ in fev) / len(fev)
     idx_bytes, topk_bytes, attn_bytes = decode_bytes(wl)
     achieved = idx_bytes / (t_idx * 1e-3) / 1e9
     step_bytes = L * (idx_bytes + topk_bytes + attn_bytes)
     log(f"indexer {t_idx * 1e3:.1f} us ({achieved:.0f} GB/s), topk {t_topk * 1e3:.1f} us, "
-        f"attention {t_attn * 1e3:.1f} us")
+        f"attention {t_attn * 1e3:.1f} us, fused topk+attention {t_fused * 1e3:.1f} us")
 
     result = {
         "metric": METRIC,
@@ -303,13 +356,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "layers": L, "ctx_len": int(wl.ctx_lens[0]),
                    "heads": H, "head_dim": 128, "block_size": 32, "topk_blocks": 16, "local_blocks": 4,
-                   "queries_per_step": B * L, "plant": wl.notes},
+                   "queries_per_step": B * L, "plant": wl.notes, "micro_batches": ns},
         "tokens_per_s": B / (ms_step * 1e-3),
         "step_hbm_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "step_algorithmic_bytes": step_bytes,
         "kernel_us": {"indexer_score_decode": t_idx * 1e3, "block_topk_decode": t_topk * 1e3,
-                      "sparse_attn_decode": t_attn * 1e3},
+                      "sparse_attn_decode": t_attn * 1e3, "topk_attn_decode": t_fused * 1e3},
+        "step_launches": "indexer_score_decode + " + ("block_topk_decode + sparse_attn_decode" if args.separate
+                                                      else "topk_attn_decode") + " per layer",
         "roofline": {"kernel": "indexer_score_decode", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "algorithmic_bytes_per_launch": idx_bytes,

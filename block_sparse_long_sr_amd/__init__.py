@@ -17,7 +17,7 @@ from typing import Optional
 
 __all__ = [
     "SparseCfg", "KV", "UocrError", "lib_path", "make_cfg", "make_kv",
-    "indexer_score_decode", "block_topk_decode", "sparse_attn_decode",
+    "indexer_score_decode", "block_topk_decode", "sparse_attn_decode", "topk_attn_decode",
     "indexer_score_prefill", "block_topk_prefill", "sparse_attn_prefill",
     "workspace_size", "status_string", "last_error", "abi_version",
     "OP_INDEXER_DECODE", "OP_TOPK_DECODE", "OP_ATTN_DECODE",
@@ -82,6 +82,7 @@ _SIGS = {
     "uocr_indexer_score_decode": ([_CFG, _KV, _P, _P, _P], ctypes.c_int),
     "uocr_block_topk_decode": ([_CFG, _P, _P, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "uocr_sparse_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "uocr_topk_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "uocr_indexer_score_prefill": ([_CFG, _KV, _P, _I32, _I32, _P, _SZ, _P], ctypes.c_int),
     "uocr_block_topk_prefill": ([_CFG, _P, _SZ, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "uocr_sparse_attn_prefill": ([_CFG, _KV, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
@@ -161,6 +162,13 @@ def block_topk_decode(cfg: SparseCfg, block_scores, ctx_lens, batch: int, max_bl
 def sparse_attn_decode(cfg: SparseCfg, kv: KV, q, block_idx, out, lse=None, ws=None, stream=None) -> None:
     _check(_lib.uocr_sparse_attn_decode(ctypes.byref(cfg), ctypes.byref(kv), _ptr(q), _ptr(block_idx), _ptr(out),
                                         _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream)), "sparse_attn_decode")
+
+
+def topk_attn_decode(cfg: SparseCfg, kv: KV, q, block_scores, block_idx, out, lse=None, n_sel=None, ws=None,
+                     stream=None) -> None:
+    _check(_lib.uocr_topk_attn_decode(ctypes.byref(cfg), ctypes.byref(kv), _ptr(q), _ptr(block_scores),
+                                      _ptr(block_idx), _ptr(n_sel), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws),
+                                      _stream(stream)), "topk_attn_decode")
 
 
 def indexer_score_prefill(cfg: SparseCfg, kv: KV, q_idx, q_start: int, T: int, cand_ws, stream=None) -> None:

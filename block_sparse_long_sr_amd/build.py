@@ -1,6 +1,7 @@
 """Build libuocr_sparse.so (gfx950) in-tree with hipcc.
 
-Usage: ``python -m block_sparse_long_sr_amd.build`` or ``build()``.  Every call
+Usage: ``python block_sparse_long_sr_amd/build.py`` (a script: the package
+itself refuses to import until the library exists) or ``build()``.  Every call
 recompiles every source; the objects go to ``_build/`` and the shared library
 next to this file, where the binding loads it.
 """

@@ -205,6 +205,52 @@ int uocr_sparse_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const
   return attn_common(cfg, kv, q, block_idx, out, lse, kv->batch, 0, 0, stream);
 }
 
+int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q,
+                          const float* block_scores, int32_t* block_idx, int32_t* n_sel, float* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;  // no workspace needed (size query returns 0)
+  TRY(check_cfg(cfg));
+  TRY(check_kv(kv, false, true));
+  if (cfg->topk_blocks > uocr::kMaxFusedTopk)
+    return fail(UOCR_EUNSUPPORTED, "fused selection + attention supports topk_blocks <= %d (got %d)",
+                uocr::kMaxFusedTopk, cfg->topk_blocks);
+  if ((int64_t)kv->max_blocks - cfg->local_blocks > uocr::kMaxFusedCandidates)
+    return fail(UOCR_EUNSUPPORTED, "fused selection + attention supports max_blocks - local_blocks <= %d",
+                uocr::kMaxFusedCandidates);
+  if (kv->batch == 0) return ok();
+  REQ_PTR4(kv->ctx_lens, "kv->ctx_lens");
+  REQ_PTR16(q, "q");
+  REQ_PTR4(block_scores, "block_scores");
+  REQ_PTR4(block_idx, "block_idx");
+  OPT_PTR4(n_sel, "n_sel");
+  REQ_PTR4(out, "out");
+  OPT_PTR4(lse, "lse");
+  uocr::SelAttnArgs sa{};
+  uocr::AttnArgs& a = sa.attn;
+  a.k_pool = kv->k_pool;
+  a.v_pool = kv->v_pool;
+  a.block_table = kv->block_table;
+  a.ctx_lens = kv->ctx_lens;
+  a.q = q;
+  a.block_idx = nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.num_blocks = kv->num_blocks;
+  a.nq = kv->batch;
+  a.heads = cfg->num_heads;
+  a.max_blocks = kv->max_blocks;
+  a.topk = cfg->topk_blocks;
+  a.scale_log2 = cfg->sm_scale * 1.44269504088896340736f;
+  a.prefill = 0;
+  a.q_start = 0;
+  sa.block_scores = block_scores;
+  sa.block_idx_out = block_idx;
+  sa.n_sel = n_sel;
+  sa.local_blocks = cfg->local_blocks;
+  return hip_status(uocr::launch_select_attn(sa, static_cast<hipStream_t>(stream)), "topk_attn_decode");
+}
+
 int uocr_indexer_score_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q_idx,
                                int32_t q_start, int32_t T, void* cand_ws, size_t cand_ws_bytes, void* stream) {
   TRY(check_cfg(cfg));

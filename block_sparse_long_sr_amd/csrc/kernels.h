@@ -56,6 +56,18 @@ struct AttnArgs {
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 
+// Fused decode selection + attention (steps 3 and 4).
+constexpr int32_t kMaxFusedTopk = 256;
+constexpr int32_t kMaxFusedCandidates = 1024 * 16;
+struct SelAttnArgs {
+  AttnArgs attn;               // prefill = 0; block_idx unused
+  const float* block_scores;   // [B][max_blocks]
+  int32_t* block_idx_out;      // [B][topk], written
+  int32_t* n_sel;              // [B] or null
+  int32_t local_blocks;
+};
+hipError_t launch_select_attn(const SelAttnArgs& a, hipStream_t stream);
+
 // Chunked-prefill scoring: partition of the context into splits.
 struct PrefillPlan {
   int32_t n_tiles;   // ceil(T / 256) row tiles

@@ -13,276 +13,35 @@
 // re-reads the scores from memory on every pass.
 #include "device_common.h"
 #include "kernels.h"
+#include "select_common.h"
 
 namespace uocr {
 
 namespace {
 
-template <int NT>
-__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
-  constexpr int kWaves = NT / kWave;
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    uint32_t o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
-  if (lane == kWave - 1) scratch[wave] = v;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    uint32_t s = scratch[w];
-    if (w < wave) before += s;
-    all += s;
-  }
-  __syncthreads();
-  *total = all;
-  return v + before;
-}
-
-// Shared prelude: trivial selections (everything, or the local window only).
-// Returns true when the row is complete.
-__device__ __forceinline__ bool topk_trivial(const TopkDecodeArgs& a, int b, int nt, int& ncand, int& R,
+// Shared prelude: query geometry, n_sel, trivial selections.  Returns true
+// when the row is complete.
+__device__ __forceinline__ bool topk_prelude(const TopkDecodeArgs& a, int b, int nt, int& ncand, int& R,
                                              int32_t*& out) {
-  const int tid = threadIdx.x;
   const int L = clamp_ctx(a.ctx_lens[b], a.max_blocks);
   const int nb = (L + kBlock - 1) / kBlock;
   ncand = nb - a.local_blocks > 0 ? nb - a.local_blocks : 0;
   R = a.topk - a.local_blocks;
   out = a.block_idx + (int64_t)b * a.topk;
-  if (a.n_sel != nullptr && tid == 0) a.n_sel[b] = nb < a.topk ? nb : a.topk;
-  if (ncand <= R) {
-    // Every block 0..nb-1 is kept (remote candidates then the local window).
-    for (int i = tid; i < a.topk; i += nt) out[i] = i < nb ? i : -1;
-    return true;
-  }
-  if (R == 0) {
-    for (int i = tid; i < a.topk; i += nt) out[i] = ncand + i;
-    return true;
-  }
-  return false;
-}
-
-}  // namespace
-
-// ---------------------------------------------------------------------------
-// Fast variant: NT threads, up to KPT candidate keys per thread in registers.
-//
-//  1. keys are loaded once, branch-free (one memory round trip);
-//  2. radix pass on the top byte: nearly every key of a score distribution
-//     shares one or two top bytes, so each wave counts one digit at a time
-//     (a uniform loop over the distinct digits it holds) and adds one wave
-//     sum per digit instead of 64 serialised same-address LDS adds;
-//  3. radix pass on the second byte among keys with the chosen top byte
-//     (spread digits: plain LDS adds);
-//  4. keys above the 16-bit prefix are kept; keys sharing it ("maybe", few)
-//     are ranked exactly by (key desc, id asc) with one counting pass; the
-//     kept ids are put in ascending order by counting.
-// When too many keys share the 16-bit prefix (heavy exact ties), or R is
-// large, it finishes with the two remaining radix passes and an ordered
-// compaction instead.
-// ---------------------------------------------------------------------------
-namespace {
-
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);
-  v += __shfl_xor(v, 16, kWave);
-  v += __shfl_xor(v, 32, kWave);
-  return v;
-}
-
-// Wave 0 finds the digit holding the `remaining`-th largest key from the
-// 256-bin histogram (bins scanned from the top digit down).
-template <int NT>
-__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t remaining, uint32_t* s_digit,
-                                           uint32_t* s_remaining) {
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    // lane holds digits 255-4*lane .. 252-4*lane (descending)
-    uint32_t c[4];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c[i] = hist[255 - 4 * lane - i];
-      sum += c[i];
-    }
-    uint32_t incl = sum;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const uint32_t o = __shfl_up(incl, d, kWave);
-      if (lane >= d) incl += o;
-    }
-    uint32_t cum = incl - sum;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t nc = cum + c[i];
-      if (nc >= remaining && cum < remaining) {
-        *s_digit = 255u - 4u * lane - i;
-        *s_remaining = remaining - cum;
-      }
-      cum = nc;
-    }
-  }
+  if (a.n_sel != nullptr && threadIdx.x == 0) a.n_sel[b] = nb < a.topk ? nb : a.topk;
+  return select_trivial(nb, ncand, R, a.topk, out, nt);
 }
 
 }  // namespace
 
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void topk_decode_reg_kernel(TopkDecodeArgs a) {
-  constexpr int kCap = 512;
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t scan_scratch[NT / kWave];
-  __shared__ uint32_t s_digit, s_remaining, s_nin, s_nmaybe;
-  __shared__ int32_t s_sel[kCap];
-  __shared__ uint64_t s_maybe[kCap];
-
+  __shared__ SelectSmem<NT> sm;
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int lane = lane_id();
   int ncand, R;
   int32_t* out;
-  if (topk_trivial(a, b, NT, ncand, R, out)) return;
-
-  const float* sc = a.block_scores + (int64_t)b * a.max_blocks;
-  uint32_t key[KPT];
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int j = tid + i * NT;
-    key[i] = __float_as_uint(sc[j < ncand ? j : ncand - 1]);
-  }
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) key[i] = (tid + i * NT < ncand) ? order_key(__uint_as_float(key[i])) : 0u;
-
-  // ---- pass A: top byte, one wave sum per distinct digit -------------------
-  if (tid < 256) hist[tid] = 0;
-  if (tid == 0) {
-    s_nin = 0;
-    s_nmaybe = 0;
-  }
-  __syncthreads();
-  {
-    uint32_t pending = 0;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) pending |= (tid + i * NT < ncand) ? (1u << i) : 0u;
-    while (__ballot(pending != 0) != 0) {
-      const uint64_t act = __ballot(pending != 0);
-      const int leader = __builtin_ctzll(act);
-      uint32_t first = 0;
-#pragma unroll
-      for (int i = KPT - 1; i >= 0; --i)
-        if (pending & (1u << i)) first = key[i] >> 24;
-      const uint32_t d = __builtin_amdgcn_readlane(first, leader);
-      uint32_t cnt = 0;
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const bool hit = (pending & (1u << i)) && (key[i] >> 24) == d;
-        cnt += hit ? 1u : 0u;
-        pending &= hit ? ~(1u << i) : ~0u;
-      }
-      cnt = wave_sum_u32(cnt);
-      if (lane == 0) atomicAdd(&hist[d], cnt);
-    }
-  }
-  __syncthreads();
-  find_digit<NT>(hist, (uint32_t)R, &s_digit, &s_remaining);
-  __syncthreads();
-  const uint32_t dA = s_digit;
-  const uint32_t remA = s_remaining;
-  __syncthreads();
-
-  // ---- pass B: second byte among keys with top byte dA ---------------------
-  if (tid < 256) hist[tid] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    if (tid + i * NT < ncand && (key[i] >> 24) == dA) atomicAdd(&hist[(key[i] >> 16) & 255u], 1u);
-  }
-  __syncthreads();
-  find_digit<NT>(hist, remA, &s_digit, &s_remaining);
-  __syncthreads();
-  const uint32_t P16 = (dA << 8) | s_digit;  // top 16 bits of the cutoff key
-  const uint32_t rem16 = s_remaining;           // slots left for keys with prefix P16
-
-  // ---- gather: keys above the prefix are in; keys on it are ranked ---------
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int j = tid + i * NT;
-    if (j < ncand) {
-      const uint32_t hi = key[i] >> 16;
-      if (hi > P16) {
-        const uint32_t pos = atomicAdd(&s_nin, 1u);  // exactly R - rem16 of them
-        if (pos < (uint32_t)kCap) s_sel[pos] = j;
-      } else if (hi == P16) {
-        const uint32_t pos = atomicAdd(&s_nmaybe, 1u);
-        if (pos < (uint32_t)kCap) s_maybe[pos] = ((uint64_t)key[i] << 32) | (0xFFFFFFFFu - (uint32_t)j);
-      }
-    }
-  }
-  __syncthreads();
-  const uint32_t nin = s_nin;
-  const uint32_t nmaybe = s_nmaybe;
-  if (R <= kCap && nmaybe <= (uint32_t)kCap) {
-    for (uint32_t e = tid; e < nmaybe; e += NT) {
-      const uint64_t my = s_maybe[e];
-      uint32_t r = 0;
-      for (uint32_t k = 0; k < nmaybe; ++k) r += s_maybe[k] > my ? 1u : 0u;
-      if (r < rem16) s_sel[nin + r] = (int32_t)(0xFFFFFFFFu - (uint32_t)my);
-    }
-    __syncthreads();
-    for (int r = tid; r < R; r += NT) {
-      const int32_t my = s_sel[r];
-      int pos = 0;
-      for (int k = 0; k < R; ++k) pos += s_sel[k] < my ? 1 : 0;
-      out[pos] = my;
-    }
-  } else {
-    // ---- fallback: radix passes on bytes 1 and 0, ordered compaction -------
-    uint32_t prefix = P16 << 16, prefix_mask = 0xFFFF0000u, remaining = rem16;
-#pragma unroll
-    for (int pass = 2; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        if (tid + i * NT < ncand && (key[i] & prefix_mask) == prefix)
-          atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      find_digit<NT>(hist, remaining, &s_digit, &s_remaining);
-      __syncthreads();
-      prefix |= s_digit << shift;
-      prefix_mask |= 255u << shift;
-      remaining = s_remaining;
-      __syncthreads();
-    }
-    const uint32_t T = prefix;
-    const uint32_t need_eq = remaining;
-    uint32_t eq_seen = 0, taken = 0;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int j = tid + i * NT;
-      const bool in = j < ncand;
-      const uint32_t eq = (in && key[i] == T) ? 1u : 0u;
-      uint32_t eq_total;
-      const uint32_t eq_incl = block_incl_scan<NT>(eq, scan_scratch, &eq_total);
-      const uint32_t eq_before = eq_seen + eq_incl - eq;
-      const uint32_t take = (in && (key[i] > T || (eq && eq_before < need_eq))) ? 1u : 0u;
-      uint32_t take_total;
-      const uint32_t take_incl = block_incl_scan<NT>(take, scan_scratch, &take_total);
-      const uint32_t pos = taken + take_incl - 1;
-      if (take && pos < (uint32_t)R) out[pos] = j;
-      eq_seen += eq_total;
-      taken += take_total;
-    }
-  }
-  // Local window after the remote ids (all larger than every candidate).
-  for (int i = tid; i < a.local_blocks; i += NT) out[R + i] = ncand + i;
+  if (topk_prelude(a, b, NT, ncand, R, out)) return;
+  select_sorted_reg<NT, KPT>(a.block_scores + (int64_t)b * a.max_blocks, ncand, R, a.local_blocks, out, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -299,7 +58,7 @@ __global__ __launch_bounds__(kGenThreads) void topk_decode_global_kernel(TopkDec
   const int tid = threadIdx.x;
   int ncand, R;
   int32_t* out;
-  if (topk_trivial(a, b, kGenThreads, ncand, R, out)) return;
+  if (topk_prelude(a, b, kGenThreads, ncand, R, out)) return;
   const float* sc = a.block_scores + (int64_t)b * a.max_blocks;
 
   uint32_t prefix = 0, prefix_mask = 0, remaining = (uint32_t)R;

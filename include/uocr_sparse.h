@@ -155,6 +155,27 @@ int uocr_sparse_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const
                             const int32_t* block_idx, float* out, float* lse, void* ws, size_t ws_bytes,
                             void* stream);
 
+/*
+ * Decode steps 3 and 4 in one launch (news.rkmt.cn/news/25027 Sec. 5 steps
+ * 3-4): the selection of uocr_block_topk_decode followed by the attention of
+ * uocr_sparse_attn_decode over it, with identical results (each head's
+ * workgroup repeats the sequence's selection, so no selection launch sits
+ * between a layer's scoring and attention).
+ *   q            : [batch][H][D] bf16
+ *   block_scores : [batch][max_blocks] float32, as uocr_indexer_score_decode
+ *                  writes them
+ *   block_idx    : [batch][topk_blocks] int32, written (the selection)
+ *   n_sel        : [batch] int32 or NULL
+ *   out, lse     : as uocr_sparse_attn_decode
+ *   ws           : workspace of uocr_workspace_size(cfg, UOCR_OP_ATTN_DECODE,
+ *                  ...) bytes (NULL allowed when that is 0)
+ * Requires topk_blocks <= 256 and max_blocks - local_blocks <= 16384;
+ * UOCR_EUNSUPPORTED otherwise (use the two separate calls).
+ */
+int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q,
+                          const float* block_scores, int32_t* block_idx, int32_t* n_sel, float* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------- chunked prefill */
 
 /*

@@ -14,10 +14,14 @@ HEADER = os.path.join(ROOT, "include", "uocr_sparse.h")
 
 
 def _ensure_built():
-    from block_sparse_long_sr_amd import build as B
     lib = os.path.join(ROOT, "block_sparse_long_sr_amd", "libuocr_sparse.so")
     if not os.path.exists(lib):
-        B.build()
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("_uocr_build", os.path.join(ROOT, "block_sparse_long_sr_amd",
+                                                                                   "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     return lib
 
 
@@ -113,12 +117,31 @@ def test_decode_argument_checks(U):
     assert e.value.status == 2
 
 
+def test_fused_decode_argument_checks(U):
+    cfg = U.make_cfg(topk_blocks=257)
+    with pytest.raises(U.UocrError) as e:
+        U.topk_attn_decode(cfg, _kv(U), FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == 5 and "topk_blocks" in U.last_error()
+    cfg = U.make_cfg()
+    with pytest.raises(U.UocrError) as e:   # 16384 remote candidates at most
+        U.topk_attn_decode(cfg, _kv(U, max_blocks=16384 + 5), FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == 5 and "max_blocks" in U.last_error()
+    with pytest.raises(U.UocrError) as e:
+        U.topk_attn_decode(cfg, _kv(U), FAKE, None, FAKE, FAKE, stream=0)
+    assert e.value.status == 1 and "block_scores" in U.last_error()
+    with pytest.raises(U.UocrError) as e:
+        U.topk_attn_decode(cfg, _kv(U), FAKE, FAKE, FAKE, None, stream=0)
+    assert e.value.status == 1 and "out" in U.last_error()
+    assert U.workspace_size(cfg, 2, 16, 4096) == 0
+
+
 def test_empty_batch_is_a_no_op(U):
     cfg = U.make_cfg()
     # batch 0: nothing to do, nothing launched, success without touching HIP
     U.indexer_score_decode(cfg, _kv(U, batch=0), None, None, stream=0)
     U.block_topk_decode(cfg, None, None, 0, 8, None, stream=0)
     U.sparse_attn_decode(cfg, _kv(U, batch=0), None, None, None, stream=0)
+    U.topk_attn_decode(cfg, _kv(U, batch=0), None, None, None, None, stream=0)
 
 
 def test_prefill_argument_checks(U):

@@ -192,3 +192,41 @@ def test_planted_query_selects_planted_blocks():
     for e in wl.edits:
         got = [int(x) for x in res["idx"][e.seq] if x >= 0]
         assert got[:12] == sorted((e.tokens // 32).tolist())
+
+
+@pytest.mark.parametrize("lens,topk,local", [
+    ([0, 1, 31, 32, 33, 127, 128, 129, 511, 512, 513, 4095, 4097], 16, 4),
+    ([32768, 20001, 9999, 700], 16, 4),
+    ([32768, 5000], 64, 4),
+    ([32768, 3000], 256, 8),
+    ([140000, 70000, 1000], 16, 4),      # > 4096 candidates: 16 keys per thread
+])
+def test_fused_select_attention_equals_separate_calls(lens, topk, local):
+    wl = _wl(f"fused {topk}", 0xE7 + topk, lens)
+    print("case: fused selection+attention", lens, topk, local, flush=True)
+    dev = SD.generate(wl)
+    cfg = G.cfg_for(wl, topk, local)
+    ref = G.gpu_decode(dev, 0, cfg)
+    B, H, D = wl.batch, wl.heads, wl.head_dim
+    scores = torch.from_numpy(ref["scores"]).cuda()
+    idx = torch.full((B, topk), -7, dtype=torch.int32, device="cuda")
+    nsel = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((B, H, D), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
+    U.topk_attn_decode(cfg, dev.kv(0), dev.q[0], scores, idx, out, lse, n_sel=nsel)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"])
+    np.testing.assert_array_equal(nsel.cpu().numpy(), ref["nsel"])
+    np.testing.assert_array_equal(out.cpu().numpy(), ref["out"])
+    np.testing.assert_array_equal(lse.cpu().numpy(), ref["lse"])
+
+
+def test_fused_select_attention_rejects_unsupported():
+    cfg = U.make_cfg(topk_blocks=300)
+    wl = _wl("fused unsupported", 0xE8, [1000])
+    dev = SD.generate(wl)
+    with pytest.raises(U.UocrError) as e:
+        U.topk_attn_decode(cfg, dev.kv(0), dev.q[0], torch.zeros(1, wl.max_blocks, device="cuda"),
+                           torch.zeros(1, 300, dtype=torch.int32, device="cuda"),
+                           torch.zeros(1, 10, 128, device="cuda"))
+    assert e.value.status == 5
