@@ -30,7 +30,7 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC"]
 SOURCES = ["api.cpp", "indexer_decode.hip", "topk_decode.hip", "attn.hip", "indexer_prefill.hip"]
 # MFMA results in ordinary VGPRs: the prefill epilogue reads every accumulator
 # with vector ALU instructions, which AGPRs would first have to be copied out of.
-PER_FILE_FLAGS = {"indexer_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+PER_FILE_FLAGS = {}
 
 
 def _run(cmd):

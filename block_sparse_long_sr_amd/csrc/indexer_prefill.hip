@@ -4,16 +4,21 @@
 // Sec. 3, on the [tokens, context/32] temporary that this kernel avoids).
 //
 // The indexer product [T x 128] . [128 x keys] is a real dense contraction.
-// Work is tiled as 256 query rows x one context split per workgroup (4 waves,
-// 64 rows each).  Per 32-key block the workgroup stages the 8 KB indexer tile
-// in LDS (rows padded to 272 B, two buffers, fetched three blocks ahead);
-// each wave multiplies it with
-// its two resident 32-row query tiles using v_mfma_f32_32x32x16_bf16 with the
-// keys on the M axis and the queries on N.  A lane then holds 16 of the 32
-// key scores of one query column, so the block max is 16 in-lane maxima and
-// one permlane32 swap.  The loop is software-pipelined: block j+1's products
-// are issued before block j's epilogue (two accumulator sets), so matrix and
-// vector work of one wave overlap.  Blocks beyond a row's causal candidate limit
+// Work is tiled as 512 query rows x one context split per workgroup of 8
+// waves, two per SIMD; each wave holds two 32-row query tiles in registers.
+// Each 32-key block's 8 KB indexer tile is copied from memory straight into
+// one of four LDS buffers (global_load_lds, three blocks ahead, 1 KB per
+// wave); each wave multiplies it with its query tiles using
+// v_mfma_f32_32x32x16_bf16 with the keys on the M axis and the queries on N.
+// A lane then holds 16 of the 32 key scores of one query column per tile,
+// and the block max is 16 in-lane maxima and one permlane32 swap, after which
+// lane half h owns the row of tile h.
+//
+// The two waves of a SIMD take turns: between consecutive barriers one of
+// them issues a block's products while the other runs the block max and list
+// insertion of the block it multiplied before (and reads the A fragments of
+// its next block from LDS), so the matrix unit stays busy while the vector
+// unit does the epilogue.  Blocks beyond a row's causal candidate limit
 // (j <= (q_start+t)/32 - local) are skipped per row.  Each lane keeps a
 // sorted list of its row's best (topk - local) blocks of the split; only
 // those lists are written, never the [T, context/32] score matrix.
@@ -26,19 +31,32 @@
 //
 // The 128-dim contraction is split into 8 MFMA steps of 16; lane half h of an
 // operand covers dims 64h + 8s .. +8 in step s for both A and B, a consistent
-// permutation of the summation order that lets every lane read 128
-// contiguous bytes.
+// permutation of the summation order.  In LDS, key row r keeps its 16-byte
+// chunk c at slot c ^ (r mod 16) of a 256-byte row, so that both the copy
+// (16 lanes per row) and the A fragment reads (one chunk of 32 rows) are free
+// of bank conflicts.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace uocr {
 
 namespace {
-constexpr int kPfThreads = 256;
-constexpr int kPfRows = 256;       // query rows per workgroup
-constexpr int kLdsRow = 272;       // bytes per staged key row (256 + 16 pad)
-constexpr int kLdsTile = kBlock * kLdsRow;
+constexpr int kPfThreads = 512;
+constexpr int kPfWaves = kPfThreads / kWave;      // 8
+constexpr int kPfRows = kPfWaves * 64;            // 512 query rows per workgroup
+constexpr int kTileBytes = kBlock * kDim * 2;     // 8 KB indexer tile
+constexpr int kMaxBps = 1 << kMaxIdBits;          // blocks per split (pool indices in LDS)
+constexpr int kAhead = 3;                         // copies run this many blocks ahead (four buffers)
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 }  // namespace
+
+// s_waitcnt with only the vector-memory counter limited to n (expcnt and
+// lgkmcnt at their maxima, no wait).
+#define UOCR_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+// s_waitcnt lgkmcnt(0) only.
+#define UOCR_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
 
 // Candidate key of a block score: the order-preserving key, at least 1, so
 // that an empty list slot (key 0) ranks below every block, NaN included.
@@ -47,28 +65,209 @@ __device__ __forceinline__ uint32_t cand_key(float f) {
   return k > 1u ? k : 1u;
 }
 
-// A fragments of one staged key tile: key n, dims 64h + 8s .. +8 (s = 0..7).
-__device__ __forceinline__ void read_a(const unsigned char* tile, int n, int h, uint4 (&a)[8]) {
-  const unsigned char* at = tile + n * kLdsRow + h * 128;
+__device__ __forceinline__ float max16(const f32x16_t& v) {
+  float m = fmaxf(fmaxf(v[0], v[1]), v[2]);
 #pragma unroll
-  for (int s = 0; s < 8; ++s) a[s] = *reinterpret_cast<const uint4*>(at + s * 16);
-}
-
-__device__ __forceinline__ void mfma_block(const uint4 (&a)[8], const uint4 (&qf)[2][8], f32x16_t& acc0,
-                                           f32x16_t& acc1) {
-  acc0 = f32x16_t{0};
-  acc1 = f32x16_t{0};
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, a[s]);
-    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, __builtin_bit_cast(bf16x8_t, qf[0][s]), acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, __builtin_bit_cast(bf16x8_t, qf[1][s]), acc1, 0, 0, 0);
-  }
+  for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, v[r]), v[r + 1]);
+  return fmaxf(m, v[15]);
 }
 
 template <int R>
-__global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kLdsTile];
+__device__ __forceinline__ void insert_sorted(uint32_t (&lk)[R], uint32_t kp) {
+#pragma unroll
+  for (int r = R - 1; r > 0; --r) lk[r] = max(lk[r], min(lk[r - 1], kp));
+  lk[0] = max(lk[0], kp);
+}
+
+// Which of the two waves of its SIMD this wave is (0 or 1, from the order in
+// which the waves of the workgroup register).  Only the overlap depends on
+// it: either role computes the same results.
+__device__ __forceinline__ int simd_turn(uint32_t* counters) {
+  // HW_ID bits 5:4 hold the SIMD of the wave.
+  const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4);
+  const uint32_t simd = (hw >> 4) & 3u;
+  uint32_t rank = 0;
+  if (lane_id() == 0) rank = atomicAdd(&counters[simd], 1u);
+  return (int)(__builtin_amdgcn_readfirstlane(rank) & 1u);
+}
+
+// The block loop of one workgroup.  The four tile buffers and the pool-index
+// table are separate LDS objects, so the compiler knows that reading one
+// buffer does not depend on copies still landing in another and leaves those
+// waits to the explicit counts below.
+template <int R>
+__device__ __forceinline__ void prefill_blocks(const IndexerPrefillArgs& a, int jb, int je, int tw, int lim,
+                                               int turn, lds_u8* __restrict__ B0, lds_u8* __restrict__ B1,
+                                               lds_u8* __restrict__ B2, lds_u8* __restrict__ B3,
+                                               lds_i32* __restrict__ tbl, const unsigned char* __restrict__ pool,
+                                               uint32_t (&lk)[R]) {
+  const PrefillPlan& P = a.plan;
+  lim = min(lim, je - 1);  // steps past the split's end keep nothing
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int h = lane >> 5;
+  const int n = lane & 31;
+
+  for (int i = tid; i < je - jb; i += kPfThreads) tbl[i] = a.block_table[jb + i];
+
+  // Resident query fragments: tile c, step s -> dims 64h + 8s .. +8 of row
+  // tw + 32c + n (rows past T read row T-1 and are never kept).
+  bf16x8_t qf[2][8];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int t = min(tw + c * 32 + n, a.T - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(a.q_idx + (int64_t)t * kDim + 64 * h);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[c][s] = __builtin_bit_cast(bf16x8_t, src[s]);
+  }
+  __syncthreads();
+
+  // Copy share of this wave: 1 KB piece `wave` of a tile, i.e. rows
+  // 4*wave + lane/16; lane reads the chunk stored at its slot.
+  const int crow = 4 * wave + (lane >> 4);
+  const uint32_t goff = (uint32_t)(crow * 256 + (((lane & 15) ^ (crow & 15)) * 16));
+  const int ldsoff = wave * 1024;
+  // A fragment of step s: row n, chunk 8h + s.
+  uint32_t raddr[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) raddr[s] = (uint32_t)(n * 256 + (((8 * h + s) ^ (n & 15)) * 16));
+
+  // Copy of block jj into buffer BUF (an invalid pool index copies pool
+  // block 0 and is flagged in okbits at bit (jj - jb) mod 64).
+  const uint32_t nb32 = a.num_blocks < 0x7FFFFFFF ? (uint32_t)a.num_blocks : 0x7FFFFFFFu;
+  uint64_t okbits = 0;
+#define UOCR_COPY(jj, BUF)                                                                                \
+  do {                                                                                                    \
+    const int k_ = (jj) - jb;                                                                             \
+    const uint32_t pb_ = (uint32_t)__builtin_amdgcn_readfirstlane(tbl[k_]);                               \
+    const bool ok_ = pb_ < nb32; /* negative indices wrap to large values */                              \
+    const unsigned char* src_ = pool + (size_t)(ok_ ? pb_ : 0u) * kTileBytes;                             \
+    __builtin_amdgcn_global_load_lds(src_ + goff, (BUF) + ldsoff, 16, 0, 0);                              \
+    const uint64_t bit_ = 1ull << (k_ & 63);                                                              \
+    okbits = (okbits & ~bit_) | (bit_ & (0ull - (uint64_t)ok_));                                          \
+  } while (0)
+#define UOCR_BARRIER()                     \
+  do {                                     \
+    __builtin_amdgcn_sched_barrier(0);     \
+    asm volatile("" ::: "memory");         \
+    __builtin_amdgcn_s_barrier();          \
+    asm volatile("" ::: "memory");         \
+    __builtin_amdgcn_sched_barrier(0);     \
+  } while (0)
+#define UOCR_READ_A(BUF)                                                      \
+  do {                                                                        \
+    _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_) av[s_] = *(lds_bf16x8*)((BUF) + raddr[s_]); \
+  } while (0)
+
+  bf16x8_t av[8];  // A fragments of the block this wave multiplies next
+  f32x16_t c0, c1;  // products of the block this wave multiplied last
+
+#define UOCR_MFMA()                                                                                       \
+  do {                                                                                                    \
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[0], qf[0][0], f32x16_t{0}, 0, 0, 0);                \
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[0], qf[1][0], f32x16_t{0}, 0, 0, 0);                \
+    _Pragma("unroll") for (int s_ = 1; s_ < 8; ++s_) {                                                    \
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s_], qf[0][s_], c0, 0, 0, 0);                      \
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s_], qf[1][s_], c1, 0, 0, 0);                      \
+    }                                                                                                     \
+    /* the products belong to this half step: keep them before its barrier */                            \
+    asm volatile("" : "+v"(c0), "+v"(c1));                                                                \
+  } while (0)
+
+  // Block max, candidate key and sorted insertion of block JJ for this
+  // lane's row from (c0, c1).
+#define UOCR_EPI(JJ)                                                                                      \
+  do {                                                                                                    \
+    const int jj_ = (JJ);                                                                                 \
+    const bool ok_ = ((okbits >> ((jj_ - jb) & 63)) & 1ull) != 0;                                        \
+    const auto sw_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(max16(c0)), __float_as_uint(max16(c1)), \
+                                                      false, false);                                     \
+    float b_ = fmaxf(__uint_as_float(sw_[0]), __uint_as_float(sw_[1]));                                  \
+    b_ = ok_ ? b_ : __builtin_nanf("");                                                                   \
+    const uint32_t idmask_ = (1u << P.idbits) - 1u;                                                      \
+    const uint32_t k_ = cand_key(b_);                                                                     \
+    /* NaN (key 1) stays above empty: the order bits are at least idmask + 1 */                          \
+    uint32_t p_ = ((k_ > idmask_ ? k_ : idmask_ + 1u) & ~idmask_) | (idmask_ - (uint32_t)(jj_ - jb));    \
+    p_ = jj_ <= lim ? p_ : 0u; /* rows past T have lim = -1 */                                            \
+    insert_sorted<R>(lk, p_);                                                                             \
+    /* the insertion belongs to this half step as well */                                                 \
+    _Pragma("unroll") for (int r_ = 0; r_ < R; ++r_) asm volatile("" : "+v"(lk[r_]));                     \
+  } while (0)
+
+  // Turn 0 multiplies block j in the first half of its step and runs its
+  // epilogue in the second; turn 1 runs block j-1's epilogue in the first
+  // half and multiplies block j in the second.  A wave starts the copy of
+  // block j+3 just before issuing block j's products and, before the barrier
+  // that ends the first half, waits for its copy of block j+1 (turn 0 has
+  // blocks j+2 and j+3 in flight after it, turn 1 only block j+2).  Buffer of
+  // block jb + k is k % 4; a buffer is refilled only after both turns have
+  // read the A fragments of its previous block.
+#define UOCR_STEP(BC, BN, BF, FIRST)                                                                      \
+  do {                                                                                                    \
+    if (turn == 0) {                                                                                      \
+      UOCR_COPY(min(j + kAhead, je - 1), BF);                                                             \
+      UOCR_MFMA();                                                                                        \
+      UOCR_WAIT_VM(kAhead - 1);                                                                           \
+      UOCR_BARRIER();                                                                                     \
+      UOCR_READ_A(BN);                                                                                    \
+      UOCR_EPI(j);                                                                                        \
+      UOCR_WAIT_LGKM0();                                                                                  \
+      UOCR_BARRIER();                                                                                     \
+    } else {                                                                                              \
+      UOCR_READ_A(BC);                                                                                    \
+      if (!(FIRST)) UOCR_EPI(j - 1);                                                                      \
+      UOCR_WAIT_VM(kAhead - 2);                                                                           \
+      UOCR_WAIT_LGKM0();                                                                                  \
+      UOCR_BARRIER();                                                                                     \
+      UOCR_COPY(min(j + kAhead, je - 1), BF);                                                             \
+      UOCR_MFMA();                                                                                        \
+      UOCR_BARRIER();                                                                                     \
+    }                                                                                                     \
+    ++j;                                                                                                  \
+  } while (0)
+
+  // Prologue: blocks jb .. jb+2 (copies past the split re-read its last
+  // block and are never used); turn 0 also reads block jb's A fragments.
+  UOCR_COPY(jb, B0);
+  UOCR_COPY(min(jb + 1, je - 1), B1);
+  UOCR_COPY(min(jb + 2, je - 1), B2);
+  UOCR_WAIT_VM(kAhead - 1);
+  UOCR_BARRIER();
+  if (turn == 0) UOCR_READ_A(B0);
+
+  int j = jb;
+  // Whole groups of four steps; steps past the split's last block compute on
+  // re-read tiles whose keys the row limit (capped at je - 1) discards.
+  UOCR_STEP(B0, B1, B3, true);
+  UOCR_STEP(B1, B2, B0, false);
+  UOCR_STEP(B2, B3, B1, false);
+  UOCR_STEP(B3, B0, B2, false);
+  while (j < je) {
+    UOCR_STEP(B0, B1, B3, false);
+    UOCR_STEP(B1, B2, B0, false);
+    UOCR_STEP(B2, B3, B1, false);
+    UOCR_STEP(B3, B0, B2, false);
+  }
+  if (turn != 0) UOCR_EPI(j - 1);
+  // No copy may still be landing in LDS when the workgroup ends.
+  UOCR_WAIT_VM(0);
+#undef UOCR_STEP
+#undef UOCR_EPI
+#undef UOCR_MFMA
+#undef UOCR_READ_A
+#undef UOCR_BARRIER
+#undef UOCR_COPY
+}
+
+template <int R>
+__global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerPrefillArgs a) {
+  // Four tile buffers as separate objects: the compiler then knows that an
+  // LDS read of one buffer never depends on a copy landing in another.
+  __shared__ __attribute__((aligned(16))) unsigned char tb0[kTileBytes], tb1[kTileBytes], tb2[kTileBytes],
+      tb3[kTileBytes];
+  __shared__ int32_t s_tbl[kMaxBps];  // pool indices of the split's blocks
+  __shared__ uint32_t s_turns[4];
 
   const PrefillPlan P = a.plan;
   // XCD-aware order: workgroup i runs on XCD i % 8; the row tiles of a split
@@ -81,16 +280,17 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPref
   const int split = group * 8 + xcd;
   if (split >= P.nsplit) return;
 
-  const int tid = threadIdx.x;
+  if (threadIdx.x < 4) s_turns[threadIdx.x] = 0u;
+  __syncthreads();
+  const int turn = simd_turn(s_turns);
+
   const int lane = lane_id();
-  const int wave = wave_id();
   const int h = lane >> 5;
   const int n = lane & 31;
-
   const int t0 = tile * kPfRows;
-  const int t_own = t0 + wave * 64 + h * 32 + n;  // row whose list this lane keeps
-  const bool row_ok = t_own < a.T;
-  const int lim_own = row_ok ? (a.q_start + t_own) / kBlock - a.local_blocks : -1;
+  const int tw = t0 + wave_id() * 64;  // first row of this wave
+  const int row = tw + h * 32 + n;     // row whose list this lane keeps (tile h)
+  const int lim = row < a.T ? (a.q_start + row) / kBlock - a.local_blocks : -1;
   const int t_last = min(t0 + kPfRows - 1, a.T - 1);
   const int lim_wg = (a.q_start + t_last) / kBlock - a.local_blocks;
   const int jb = split * P.bps;
@@ -100,146 +300,14 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPref
   uint32_t lk[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) lk[r] = 0u;
-
   if (jb < je) {
-    // Resident query fragments: tile c, step s -> dims 64h + 8s .. +8 of row
-    // t0 + 64*wave + 32c + n (rows past T read row T-1 and are never kept).
-    uint4 qf[2][8];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int t = min(t0 + wave * 64 + c * 32 + n, a.T - 1);
-      const uint4* src = reinterpret_cast<const uint4*>(a.q_idx + (int64_t)t * kDim + 64 * h);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) qf[c][s] = src[s];
-    }
-
-    // Staging: thread tid moves uint4 numbers tid and 256 + tid of an 8 KB
-    // key tile into the padded rows of one of two LDS buffers.  Tiles are
-    // fetched into a four-slot register ring three blocks before they are
-    // staged, so about three blocks of matrix work hide each fetch.
-    const int st0 = (tid >> 4) * kLdsRow + (tid & 15) * 16;
-    const int st1 = ((256 + tid) >> 4) * kLdsRow + (tid & 15) * 16;
-    // Branch-free fetch (an invalid pool index reads pool block 0 and is
-    // flagged), so the number of loads in flight is the same on every path
-    // and the wait before staging only covers the block being staged.
-#define UOCR_FETCH(jj, Y0, Y1, OK)                                                                        \
-  do {                                                                                                    \
-    const int pb_ = __builtin_amdgcn_readfirstlane(a.block_table[(jj)]);                                  \
-    OK = pb_ >= 0 && (int64_t)pb_ < a.num_blocks;                                                         \
-    const uint4* src_ = reinterpret_cast<const uint4*>(a.kidx_pool + (int64_t)(OK ? pb_ : 0) * (kBlock * kDim)); \
-    Y0 = src_[tid];                                                                                       \
-    Y1 = src_[256 + tid];                                                                                 \
-  } while (0)
-#define UOCR_STAGE(BUF, Y0, Y1)                                                        \
-  do {                                                                                 \
-    unsigned char* dst_ = lds + (BUF) * kLdsTile;                                      \
-    *reinterpret_cast<uint4*>(dst_ + st0) = Y0;                                        \
-    *reinterpret_cast<uint4*>(dst_ + st1) = Y1;                                        \
-  } while (0)
-
-    // Bit (k mod 64) of `okbits` says whether block jb + k has a valid pool
-    // index; it is written when the block is fetched and read at its epilogue.
-    uint64_t okbits = 0;
-    uint4 r0a, r0b, r1a, r1b, r2a, r2b, r3a, r3b;
-    {
-      uint4 t0, t1;
-      bool ok;
-      UOCR_FETCH(jb, t0, t1, ok);
-      okbits |= ok ? 1ull : 0ull;
-      UOCR_STAGE(0, t0, t1);
-      UOCR_FETCH(min(jb + 1, je - 1), t0, t1, ok);
-      okbits |= ok ? 2ull : 0ull;
-      UOCR_STAGE(1, t0, t1);
-      // Fetches past the split re-read its last block; they are never used.
-      UOCR_FETCH(min(jb + 2, je - 1), r2a, r2b, ok);
-      okbits |= ok ? 4ull : 0ull;
-      UOCR_FETCH(min(jb + 3, je - 1), r3a, r3b, ok);
-      okbits |= ok ? 8ull : 0ull;
-      UOCR_FETCH(min(jb + 4, je - 1), r0a, r0b, ok);
-      okbits |= ok ? 16ull : 0ull;
-    }
-    __syncthreads();
-
-    uint4 av[8];
-    f32x16_t accA0, accA1, accB0, accB1;
-    read_a(lds, n, h, av);
-    mfma_block(av, qf, accA0, accA1);
-
-    int j = jb;
-    // One block: fetch block j+5 into ring slot (j+5)%4, issue block j+1's
-    // products, run block j's epilogue, stage block j+2 from ring slot
-    // (j+2)%4 into LDS buffer j%2.  Block j+1's products come first (on the
-    // last block they recompute a staged tile and are never read), in one
-    // branch-free region with block j's epilogue so that the scheduler can
-    // interleave the matrix instructions with the vector ones.
-#define UOCR_STEP(LDA, LDB, STA, STB, BUF_MFMA, BUF_STAGE, CUR0, CUR1, NXT0, NXT1)                       \
-  do {                                                                                                    \
-    const int k_ = j - jb;                                                                                \
-    {                                                                                                     \
-      bool okf_;                                                                                          \
-      UOCR_FETCH(min(j + 5, je - 1), LDA, LDB, okf_);                                                    \
-      const uint64_t bit_ = 1ull << ((k_ + 5) & 63); /* reused 64 blocks later only */                    \
-      okbits = okf_ ? (okbits | bit_) : (okbits & ~bit_);                                                 \
-    }                                                                                                     \
-    read_a(lds + (BUF_MFMA) * kLdsTile, n, h, av);                                                        \
-    mfma_block(av, qf, NXT0, NXT1);                                                                       \
-    epilogue(CUR0, CUR1, ((okbits >> (k_ & 63)) & 1ull) != 0);                                            \
-    _Pragma("unroll") for (int i_ = 0; i_ < 16; ++i_) {                                                   \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* one MFMA */                                   \
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0); /* then up to five VALU */                       \
-    }                                                                                                     \
-    if (j + 2 < je) UOCR_STAGE(BUF_STAGE, STA, STB);                                                     \
-    __syncthreads();                                                                                      \
-    ++j;                                                                                                  \
-  } while (0)
-
-    // Block max, candidate key and sorted insertion of block j for this lane's row.
-    auto epilogue = [&](const f32x16_t& cur0, const f32x16_t& cur1, bool ok) __attribute__((always_inline)) {
-      float pm0 = cur0[0], pm1 = cur1[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) {
-        pm0 = fmaxf(pm0, cur0[r]);
-        pm1 = fmaxf(pm1, cur1[r]);
-      }
-      // Lanes 0-31 end with tile 0's block max of column n, lanes 32-63 with
-      // tile 1's: permlane32_swap pairs each half with the other half.
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm0), __float_as_uint(pm1), false, false);
-      float bsc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      if (!ok) bsc = __builtin_nanf("");
-      // Packed candidate: order bits of the score above `idbits`, the
-      // in-split index below (complemented, so the lower block id ranks first
-      // among equal truncated scores).  Packed keys of one split are distinct,
-      // so inserting into the sorted list is new[r] = med3(L[r], L[r-1], k).
-      const uint32_t key = cand_key(bsc);
-      const uint32_t idmask = (1u << P.idbits) - 1u;
-      const uint32_t kbase = key > idmask ? key : idmask + 1u;  // NaN (key 1) stays above empty
-      uint32_t kp = (kbase & ~idmask) | (idmask - (uint32_t)(j - jb));
-      kp = j <= lim_own ? kp : 0u;  // rows past T have lim_own = -1
-#pragma unroll
-      for (int r = R - 1; r > 0; --r) lk[r] = max(lk[r], min(lk[r - 1], kp));
-      lk[0] = max(lk[0], kp);
-    };
-
-    // Ring slot of block jb + m is m % 4; LDS buffer is m % 2.
-    while (true) {
-      UOCR_STEP(r1a, r1b, r2a, r2b, 1, 0, accA0, accA1, accB0, accB1);  // m = 0 mod 4
-      if (j >= je) break;
-      UOCR_STEP(r2a, r2b, r3a, r3b, 0, 1, accB0, accB1, accA0, accA1);  // m = 1
-      if (j >= je) break;
-      UOCR_STEP(r3a, r3b, r0a, r0b, 1, 0, accA0, accA1, accB0, accB1);  // m = 2
-      if (j >= je) break;
-      UOCR_STEP(r0a, r0b, r1a, r1b, 0, 1, accB0, accB1, accA0, accA1);  // m = 3
-      if (j >= je) break;
-    }
-#undef UOCR_STEP
-#undef UOCR_STAGE
-#undef UOCR_FETCH
+    prefill_blocks<R>(a, jb, je, tw, lim, turn, (lds_u8*)tb0, (lds_u8*)tb1, (lds_u8*)tb2, (lds_u8*)tb3,
+                      (lds_i32*)s_tbl, reinterpret_cast<const unsigned char*>(a.kidx_pool), lk);
   }
-
-  if (row_ok) {
-    const size_t off = ((size_t)t_own * P.nsplit + split) * R;
+  if (row < a.T) {
+    uint32_t* dst = a.cand_keys + ((size_t)row * P.nsplit + split) * R;
 #pragma unroll
-    for (int r = 0; r < R; ++r) a.cand_keys[off + r] = lk[r];
+    for (int r = 0; r < R; ++r) dst[r] = lk[r];
   }
 }
 
@@ -254,9 +322,11 @@ PrefillPlan prefill_plan(int32_t T, int32_t max_blocks, int32_t topk, int32_t lo
     p.ws_bytes = 0;
     return p;
   }
-  // ~512 workgroups, at least 16 blocks per split, at most 64 splits.
-  int64_t bps = ((int64_t)max_blocks * p.n_tiles + 511) / 512;
+  // About one workgroup per compute unit (more for long chunks), 16 to
+  // kMaxBps blocks per split, at most 64 splits (max_blocks <= 64 * kMaxBps).
+  int64_t bps = ((int64_t)max_blocks * p.n_tiles + 255) / 256;
   if (bps < 16) bps = 16;
+  if (bps > kMaxBps) bps = kMaxBps;
   const int64_t min_bps = ((int64_t)max_blocks + 63) / 64;
   if (bps < min_bps) bps = min_bps;
   p.bps = (int32_t)bps;
