@@ -160,16 +160,26 @@ def run_prefill(U, SD, W, torch, iters=5):
     t_sc = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(2, iters + 2)) / iters
     t_mg = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(2, iters + 2)) / iters
     t_at = sum(ev[i][2].elapsed_time(ev[i][3]) for i in range(2, iters + 2)) / iters
+    # Scoring kernel alone: one event pair around back-to-back launches.
+    nrep = 10
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_.record(stream)
+    for _ in range(nrep):
+        U.indexer_score_prefill(cfg, kv, dev.q_idx, wl.q_start, T, wsarg, stream=sh)
+    b_.record(stream)
+    torch.cuda.synchronize()
+    t_sc_alone = a_.elapsed_time(b_) / nrep
     # algorithmic work of the scoring kernel: every candidate (row, block) pair
     rowblocks = sum(max(0, (wl.q_start + t) // 32 + 1 - 4) for t in range(T))
     flops = rowblocks * 32 * 128 * 2
-    tflops = flops / (t_sc * 1e-3) / 1e12
+    tflops = flops / (t_sc_alone * 1e-3) / 1e12
     attn_unique = int(wl.ctx_lens[0]) * 10 * 128 * 2 * 2
     res = {
         "workload": wl.name,
         "rows": T,
         "tokens_per_s": T / ((t_sc + t_mg + t_at) * 1e-3),
-        "ms": {"scoring": t_sc, "merge": t_mg, "attention": t_at},
+        "ms": {"scoring": t_sc, "merge": t_mg, "attention": t_at, "scoring_back_to_back": t_sc_alone},
+        "scoring_in_step_TFLOPs": flops / (t_sc * 1e-3) / 1e12,
         "scoring_roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS,
                              "flops_per_launch": flops, "traffic": None},
@@ -186,6 +196,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one decode step as a HIP graph and time its replays")
     ap.add_argument("--separate", action="store_true",
                     help="run selection and attention as two launches instead of the fused one")
     ap.add_argument("--streams", type=int, default=2,
@@ -257,7 +269,7 @@ def main():
         for l in range(L):
             gkv.append(U.make_kv(dev.k[l], dev.v[l], dev.kidx[l], dev.block_table[b0:b1], dev.ctx_lens[b0:b1],
                                  wl.pool_blocks, b1 - b0, M))
-        groups.append((b0, b1, gkv, torch.cuda.Stream() if ns > 1 else stream))
+        groups.append((b0, b1, gkv, torch.cuda.Stream() if ns > 1 or args.graph else stream))
 
     def step():
         for l in range(L):
@@ -273,32 +285,50 @@ def main():
                     U.topk_attn_decode(cfg, gkv[l], dev.q[l, b0:b1], scores[l, b0:b1], idx[l, b0:b1],
                                        out[l, b0:b1], lse[l, b0:b1], stream=h_)
 
-    def fork():
+    def fork(base):
         ev = torch.cuda.Event()
-        ev.record(stream)
+        ev.record(base)
         for _, _, _, st in groups:
-            if st is not stream:
+            if st is not base:
                 st.wait_event(ev)
 
-    def join():
+    def join(base):
         for _, _, _, st in groups:
-            if st is not stream:
+            if st is not base:
                 ev = torch.cuda.Event()
                 ev.record(st)
-                stream.wait_event(ev)
+                base.wait_event(ev)
 
-    fork()
+    fork(stream)
     for _ in range(args.warmup):
         step()
-    join()
+    join(stream)
     torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        # One step (12 layers of every micro-batch group) captured as a HIP
+        # graph; each replay relaunches all of its kernels on the same inputs.
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        with torch.cuda.graph(graph, stream=cap):
+            fork(cap)
+            step()
+            join(cap)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    fork()
-    for _ in range(args.steps):
-        step()
-    join()
+    if graph is not None:
+        for _ in range(args.steps):
+            graph.replay()
+    else:
+        fork(stream)
+        for _ in range(args.steps):
+            step()
+        join(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
@@ -306,35 +336,29 @@ def main():
     qh_per_s = B * L * H * args.steps / (ms_total * 1e-3)
     log(f"decode step {ms_step * 1e3:.1f} us, {qh_per_s / 1e6:.3f} M query-heads/s")
 
-    # Per-kernel durations with events bracketing each launch (separate pass).
+    # Per-kernel durations (separate pass, one stream, whole batch): one event
+    # pair around the 12 back-to-back launches of a kernel (one per layer), so
+    # that the average per launch is the kernel's own duration plus the short
+    # dispatch gap between consecutive launches on a stream.
     ksteps = max(3, min(10, args.steps))
-    evs = []
-    for _ in range(ksteps):
-        for l in range(L):
-            a, b_, c, d = (torch.cuda.Event(enable_timing=True) for _ in range(4))
-            a.record(stream)
-            U.indexer_score_decode(cfg, kvs[l], dev.q_idx[l], scores[l], stream=sh)
-            b_.record(stream)
-            U.block_topk_decode(cfg, scores[l], dev.ctx_lens, B, M, idx[l], stream=sh)
-            c.record(stream)
-            U.sparse_attn_decode(cfg, kvs[l], dev.q[l], idx[l], out[l], lse[l], stream=sh)
-            d.record(stream)
-            evs.append((a, b_, c, d))
-    torch.cuda.synchronize()
-    n = len(evs)
-    t_idx = sum(a.elapsed_time(b_) for a, b_, _, _ in evs) / n
-    t_topk = sum(b_.elapsed_time(c) for _, b_, c, _ in evs) / n
-    t_attn = sum(c.elapsed_time(d) for _, _, c, d in evs) / n
-    fev = []
-    for _ in range(ksteps):
-        for l in range(L):
+
+    def timed(launch):
+        pairs = []
+        for _ in range(ksteps):
             a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a_.record(stream)
-            U.topk_attn_decode(cfg, kvs[l], dev.q[l], scores[l], idx[l], out[l], lse[l], stream=sh)
+            for l in range(L):
+                launch(l)
             b_.record(stream)
-            fev.append((a_, b_))
-    torch.cuda.synchronize()
-    t_fused = sum(a_.elapsed_time(b_) for a_, b_ in fev) / len(fev)
+            pairs.append((a_, b_))
+        torch.cuda.synchronize()
+        return sum(a_.elapsed_time(b_) for a_, b_ in pairs) / (len(pairs) * L)
+
+    t_idx = timed(lambda l: U.indexer_score_decode(cfg, kvs[l], dev.q_idx[l], scores[l], stream=sh))
+    t_topk = timed(lambda l: U.block_topk_decode(cfg, scores[l], dev.ctx_lens, B, M, idx[l], stream=sh))
+    t_attn = timed(lambda l: U.sparse_attn_decode(cfg, kvs[l], dev.q[l], idx[l], out[l], lse[l], stream=sh))
+    t_fused = timed(lambda l: U.topk_attn_decode(cfg, kvs[l], dev.q[l], scores[l], idx[l], out[l], lse[l],
+                                                 stream=sh))
     idx_bytes, topk_bytes, attn_bytes = decode_bytes(wl)
     achieved = idx_bytes / (t_idx * 1e-3) / 1e9
     step_bytes = L * (idx_bytes + topk_bytes + attn_bytes)
@@ -356,7 +380,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "layers": L, "ctx_len": int(wl.ctx_lens[0]),
                    "heads": H, "head_dim": 128, "block_size": 32, "topk_blocks": 16, "local_blocks": 4,
-                   "queries_per_step": B * L, "plant": wl.notes, "micro_batches": ns},
+                   "queries_per_step": B * L, "plant": wl.notes, "micro_batches": ns, "hip_graph": bool(args.graph)},
         "tokens_per_s": B / (ms_step * 1e-3),
         "step_hbm_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -387,8 +411,10 @@ def main():
     if not args.no_prefill:
         log("chunked prefill T=2048 at 129024 of 131072")
         result["prefill"] = run_prefill(U, SD, W, torch)
-        log(f"prefill scoring {result['prefill']['ms']['scoring'] * 1e3:.1f} us "
-            f"({result['prefill']['scoring_roofline']['achieved']:.0f} TFLOP/s)")
+        pf = result["prefill"]
+        log(f"prefill scoring {pf['ms']['scoring_back_to_back'] * 1e3:.1f} us back to back "
+            f"({pf['scoring_roofline']['achieved']:.0f} TFLOP/s), {pf['ms']['scoring'] * 1e3:.1f} us in the "
+            f"chunk step; merge {pf['ms']['merge'] * 1e3:.1f} us; attention {pf['ms']['attention'] * 1e3:.1f} us")
 
     print(json.dumps(result), flush=True)
 
