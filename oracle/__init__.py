@@ -37,6 +37,7 @@ from .sr_swa import (  # noqa: F401
     indexer_scores,
     block_maxima,
     rank_candidates,
+    page_tiers,
     select_blocks,
     attended_tokens,
     attend,

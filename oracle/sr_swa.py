@@ -33,6 +33,13 @@ Readings taken where the pages leave a point open:
   of a kept block past p are not attended.
 * Output order: kept block ids ascending.  Attention output in float64 with
   its log-sum-exp; over an empty token set the output is 0 and lse = -inf.
+* Page-aware candidates (optional; [rkmt] Sec. 5 on the page-aware candidate
+  constraint, [lehvn] Sec. 2 route A on the Page Gate): the candidate domain
+  is the query's own page's image blocks plus the local window plus a global
+  fallback.  Read as a two-tier ranking of the remote candidates: blocks that
+  hold image tokens of the query's page come first (score descending, lower
+  id first), and the other candidates fill the slots they leave, in the same
+  order.  Block tags and the query's page are inputs.
 """
 from __future__ import annotations
 
@@ -112,35 +119,52 @@ def block_maxima(scores: np.ndarray, p: int, nblk: int, cfg: SparseCfg) -> np.nd
     return out
 
 
-def rank_candidates(block_scores: np.ndarray) -> np.ndarray:
+def page_tiers(block_page: Sequence[int], query_page: int, ncand: int) -> np.ndarray:
+    """Tier of each remote candidate under the page-aware constraint ([rkmt]
+    Sec. 5; [lehvn] Sec. 2 route A): 1 for a block tagged with the query's
+    page (it holds image tokens of that page), 0 for every other block."""
+    tags = np.asarray(block_page, dtype=np.int64)[:ncand]
+    return (tags == int(query_page)).astype(np.int64)
+
+
+def rank_candidates(block_scores: np.ndarray, tiers=None) -> np.ndarray:
     """Candidate ids in rank order: score descending, lower id first on ties,
     NaN last ([rkmt] Sec. 5 step 3, with the tie rule stated above)."""
     s = np.asarray(block_scores, dtype=np.float64)
     ids = np.arange(s.size)
     is_nan = np.isnan(s)
     neg = np.where(is_nan, 0.0, -s)
-    # lexsort: last key is primary.
-    return np.lexsort((ids, neg, is_nan)).astype(np.int64)
+    if tiers is None:
+        # lexsort: last key is primary.
+        return np.lexsort((ids, neg, is_nan)).astype(np.int64)
+    # Page-aware: the tier (higher first) comes before everything else.
+    neg_tier = -np.asarray(tiers, dtype=np.int64)[: s.size]
+    return np.lexsort((ids, neg, is_nan, neg_tier)).astype(np.int64)
 
 
-def select_blocks(block_scores: np.ndarray, p: int, cfg: SparseCfg) -> Dict[str, object]:
+def select_blocks(block_scores: np.ndarray, p: int, cfg: SparseCfg, tiers=None) -> Dict[str, object]:
     """Kept blocks of the query at position p ([rkmt] Sec. 5 step 3).
 
     block_scores: float32 scores of the candidate blocks 0..ncand-1.
+    tiers: optional page-aware tiers of the candidates (``page_tiers``).
     Returns a dict with ``selected`` (ascending ids), ``remote``, ``local``,
     ``ranked`` (candidates in rank order) and ``cutoff`` (score of the last
-    remote block kept by ranking, or None when every candidate is kept).
+    remote block kept by ranking, or None when every candidate is kept; with
+    tiers, ``cutoff_tier`` is that block's tier).
     """
     local = local_blocks(p, cfg)
     ncand = candidate_count(p, cfg)
     bs = np.asarray(block_scores, dtype=np.float32)[:ncand]
-    ranked = rank_candidates(bs)
+    ranked = rank_candidates(bs, tiers)
+    cutoff_tier = None
     if ncand <= cfg.remote_slots:
         remote = list(range(ncand))
         cutoff = None
     else:
         remote = sorted(int(j) for j in ranked[: cfg.remote_slots])
         cutoff = float(bs[ranked[cfg.remote_slots - 1]])
+        if tiers is not None:
+            cutoff_tier = int(np.asarray(tiers)[ranked[cfg.remote_slots - 1]])
     return {
         "selected": sorted(remote + local),
         "remote": remote,
@@ -148,6 +172,8 @@ def select_blocks(block_scores: np.ndarray, p: int, cfg: SparseCfg) -> Dict[str,
         "ranked": ranked,
         "cutoff": cutoff,
         "block_scores": bs,
+        "tiers": None if tiers is None else np.asarray(tiers, dtype=np.int64)[:ncand],
+        "cutoff_tier": cutoff_tier,
     }
 
 
@@ -186,7 +212,7 @@ def attend(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
 
 
 def decode_query(q_bits, q_idx_bits, k_bits, v_bits, kidx_bits, ctx_len: int,
-                 cfg: SparseCfg = SparseCfg()):
+                 cfg: SparseCfg = SparseCfg(), block_page=None, query_page=None):
     """One decode query of one sequence and layer, steps 1-4 in order.
 
     The query's own K/V are already in the cache, so it sits at
@@ -194,16 +220,19 @@ def decode_query(q_bits, q_idx_bits, k_bits, v_bits, kidx_bits, ctx_len: int,
     [>=ctx_len, Di]; q_bits [H, D]; q_idx_bits [Di].
     """
     return decode_query_fetch(q_bits, q_idx_bits, kidx_bits,
-                              lambda toks: (k_bits[:, toks, :], v_bits[:, toks, :]), ctx_len, cfg)
+                              lambda toks: (k_bits[:, toks, :], v_bits[:, toks, :]), ctx_len, cfg,
+                              block_page, query_page)
 
 
 def decode_query_fetch(q_bits, q_idx_bits, kidx_bits, fetch_kv, ctx_len: int,
-                       cfg: SparseCfg = SparseCfg()):
+                       cfg: SparseCfg = SparseCfg(), block_page=None, query_page=None):
     """``decode_query`` with K/V supplied on demand.
 
     ``fetch_kv(tokens)`` returns (K, V) bf16 bits [H, len(tokens), D] of the
     given token positions; only the attended tokens are ever requested, so
-    callers need not materialise a whole 128K-token cache.
+    callers need not materialise a whole 128K-token cache.  With
+    ``block_page`` (page tag per block, -1 for blocks without image tokens)
+    and ``query_page`` the page-aware ranking is used.
     """
     H, D = np.asarray(q_bits).shape
     if ctx_len <= 0:
@@ -214,7 +243,8 @@ def decode_query_fetch(q_bits, q_idx_bits, kidx_bits, fetch_kv, ctx_len: int,
     ncand = candidate_count(p, cfg)
     scores = indexer_scores(q_idx_bits, kidx_bits[: ncand * cfg.block_size])
     bscores = block_maxima(scores, p, ncand, cfg)
-    sel = select_blocks(bscores, p, cfg)
+    tiers = None if block_page is None else page_tiers(block_page, query_page, ncand)
+    sel = select_blocks(bscores, p, cfg, tiers)
     toks = attended_tokens(sel["selected"], p, cfg)
     k_rows, v_rows = fetch_kv(toks)
     out, lse = attend(q_bits, k_rows, v_rows, np.arange(toks.size), cfg.sm_scale)
@@ -223,24 +253,29 @@ def decode_query_fetch(q_bits, q_idx_bits, kidx_bits, fetch_kv, ctx_len: int,
 
 
 def prefill_rows(q_bits, q_idx_bits, k_bits, v_bits, kidx_bits, q_start: int,
-                 rows: Sequence[int], cfg: SparseCfg = SparseCfg()):
+                 rows: Sequence[int], cfg: SparseCfg = SparseCfg(), block_page=None, row_pages=None):
     """Chunked prefill: rows t of a chunk starting at q_start.
 
     Row t is the query at p = q_start + t; the chunk's own K/V are already in
     the cache and each row sees keys 0..p ([lehvn] Sec. 3 describes the
     chunked prefill; the per-row rule is the decode rule at that position).
-    q_bits [T, H, D], q_idx_bits [T, Di].  Returns one dict per row.
+    q_bits [T, H, D], q_idx_bits [T, Di].  ``row_pages[t]`` is row t's page
+    when ``block_page`` turns the page-aware ranking on.  Returns one dict
+    per row.
     """
     return prefill_rows_fetch(q_bits, q_idx_bits, kidx_bits,
-                              lambda toks: (k_bits[:, toks, :], v_bits[:, toks, :]), q_start, rows, cfg)
+                              lambda toks: (k_bits[:, toks, :], v_bits[:, toks, :]), q_start, rows, cfg,
+                              block_page, row_pages)
 
 
 def prefill_rows_fetch(q_bits, q_idx_bits, kidx_bits, fetch_kv, q_start: int,
-                       rows: Sequence[int], cfg: SparseCfg = SparseCfg()):
+                       rows: Sequence[int], cfg: SparseCfg = SparseCfg(), block_page=None, row_pages=None):
     """``prefill_rows`` with K/V supplied on demand (see decode_query_fetch)."""
     res = []
     for t in rows:
-        r = decode_query_fetch(q_bits[t], q_idx_bits[t], kidx_bits, fetch_kv, q_start + t + 1, cfg)
+        qp = None if block_page is None else int(row_pages[t])
+        r = decode_query_fetch(q_bits[t], q_idx_bits[t], kidx_bits, fetch_kv, q_start + t + 1, cfg,
+                               block_page, qp)
         r["row"] = t
         res.append(r)
     return res

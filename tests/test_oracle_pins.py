@@ -176,6 +176,119 @@ def test_nan_ranks_last_and_signed_zero_ties():
 
 
 # --------------------------------------------------------------------------
+# Page-aware candidate ranking (optional tiers)
+# --------------------------------------------------------------------------
+
+def test_page_gate_golden():
+    g = _read_pairs("page_gate.txt")
+    for suf in ("", "2"):
+        p = int(g["p" + suf][0])
+        qpage = int(g["query_page" + suf][0])
+        tags = [int(x) for x in g["tags" + suf]]
+        scores = np.array([float(x) for x in g["scores" + suf]], np.float32)
+        ncand = oracle.candidate_count(p, CFG)
+        sel = oracle.select_blocks(scores, p, CFG, oracle.page_tiers(tags, qpage, ncand))
+        assert sel["remote"] == [int(x) for x in g["remote" + suf]]
+        if "selected" + suf in g:
+            assert sel["selected"] == [int(x) for x in g["selected" + suf]]
+        assert sel["cutoff"] == float(g["cutoff" + suf][0])
+        assert sel["cutoff_tier"] == int(g["cutoff_tier" + suf][0])
+
+
+def brute_force_remote_tiered(scores, tags, qpage, n_remote):
+    """Subset of size n_remote maximising sum(score + M * [tag == qpage]) with a
+    weight M larger than any difference of score sums, exact; among equal
+    sums the lexicographically smallest sorted id tuple.  Independent of
+    sorting and of the oracle's tier helper."""
+    ex = [_exact(s) for s in scores]
+    big = 2 * sum(abs(e) for e in ex) + 1
+    w = [ex[i] + (big if tags[i] == qpage else 0) for i in range(len(scores))]
+    best, best_sum = None, None
+    for comb in itertools.combinations(range(len(scores)), n_remote):
+        s = sum(w[i] for i in comb)
+        if best_sum is None or s > best_sum or (s == best_sum and comb < best):
+            best, best_sum = comb, s
+    return list(best)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_page_gate_brute_force(seed):
+    g = np.random.default_rng(3000 + seed)
+    ncand = int(g.integers(13, 18))
+    p = (ncand + CFG.local_blocks) * CFG.block_size - 1 - int(g.integers(0, 32))
+    assert oracle.candidate_count(p, CFG) == ncand
+    # page tags: a few pages, -1 for blocks without image tokens; the query's
+    # page tags fewer or more candidates than the 12 remote slots
+    npages = int(g.integers(1, 4))
+    tags = g.integers(-1, npages, ncand).tolist()
+    qpage = int(g.integers(0, npages))
+    if seed % 3 == 0:
+        tags = [qpage if g.random() < 0.85 else -1 for _ in range(ncand)]
+    if seed % 2:
+        scores = g.integers(-3, 4, ncand).astype(np.float32)
+    else:
+        scores = g.standard_normal(ncand).astype(np.float32)
+    sel = oracle.select_blocks(scores, p, CFG, oracle.page_tiers(tags, qpage, ncand))
+    assert sel["remote"] == brute_force_remote_tiered(scores, tags, qpage, CFG.remote_slots)
+    assert sel["selected"] == sorted(sel["remote"] + oracle.local_blocks(p, CFG))
+
+
+@pytest.mark.parametrize("p", [700, 5000, 131071])
+def test_page_gate_uniform_tiers_reduce_to_plain_ranking(p):
+    g = np.random.default_rng(p)
+    ncand = oracle.candidate_count(p, CFG)
+    scores = g.standard_normal(ncand).astype(np.float32)
+    plain = oracle.select_blocks(scores, p, CFG)
+    for tags, qpage in (([3] * ncand, 3), ([-1] * ncand, 0), ([1] * ncand, 2)):
+        gated = oracle.select_blocks(scores, p, CFG, oracle.page_tiers(tags, qpage, ncand))
+        assert gated["selected"] == plain["selected"]
+        assert gated["cutoff"] == plain["cutoff"]
+
+
+def test_page_gate_in_page_blocks_first():
+    g = np.random.default_rng(11)
+    p = 4096 * 32 - 1
+    ncand = oracle.candidate_count(p, CFG)
+    scores = g.standard_normal(ncand).astype(np.float32)
+    for n_in in (0, 5, 12, 40):
+        tags = np.full(ncand, -1)
+        tags[g.choice(ncand, n_in, replace=False)] = 4
+        sel = oracle.select_blocks(scores, p, CFG, oracle.page_tiers(tags, 4, ncand))
+        inpage = set(np.nonzero(tags == 4)[0].tolist())
+        remote = set(sel["remote"])
+        if n_in <= 12:
+            assert inpage <= remote                       # all of the page's blocks kept
+            rest = sorted(set(range(ncand)) - inpage, key=lambda j: (-scores[j], j))
+            assert remote - inpage == set(rest[: 12 - n_in])   # fallback: best of the rest
+        else:
+            assert remote <= inpage                       # only the page's blocks
+            best = sorted(inpage, key=lambda j: (-scores[j], j))[:12]
+            assert remote == set(best)
+
+
+def test_page_gate_prefill_rows_use_their_own_page():
+    g = np.random.default_rng(21)
+    S, T, q_start = 3000, 64, 2936
+    ki = g.integers(-2, 3, (S, 128)).astype(np.float32)
+    kib = (ki.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    qi = g.integers(-2, 3, (T, 128)).astype(np.float32)
+    qib = (qi.view(np.uint32) >> 16).astype(np.uint16)
+    q = np.zeros((T, 10, 128), np.uint16)
+    k = np.zeros((10, S, 128), np.uint16)
+    nblk = (S + 31) // 32
+    tags = [(j * 32) // 1000 if (j * 32) % 1000 < 400 else -1 for j in range(nblk)]
+    row_pages = [(q_start + t) // 1000 for t in range(T)]
+    res = oracle.prefill_rows(q, qib, k, k, kib, q_start, [0, 63], CFG, tags, row_pages)
+    for r in res:
+        p = q_start + r["row"]
+        ncand = oracle.candidate_count(p, CFG)
+        one = oracle.decode_query(q[r["row"]], qib[r["row"]], k, k, kib, p + 1, CFG, tags, row_pages[r["row"]])
+        assert r["selected"] == one["selected"]
+        tiers = oracle.page_tiers(tags, row_pages[r["row"]], ncand)
+        assert r["tiers"].tolist() == tiers.tolist()
+
+
+# --------------------------------------------------------------------------
 # Indexer scores and block maxima
 # --------------------------------------------------------------------------
 
@@ -414,10 +527,14 @@ def test_prefill_rows_causal_and_dense():
 def _mutants():
     import oracle.sr_swa as m
 
-    def wrong_tie(scores):
+    def wrong_tie(scores, tiers=None):
         s = np.asarray(scores, np.float64)
         ids = np.arange(s.size)
         return np.lexsort((-ids, -np.nan_to_num(s), np.isnan(s)))
+
+    def reversed_tiers(block_page, query_page, ncand):
+        tags = np.asarray(block_page, dtype=np.int64)[:ncand]
+        return (tags != int(query_page)).astype(np.int64)
 
     def off_by_one_tokens(selected, p, cfg):
         toks = []
@@ -443,6 +560,7 @@ def _mutants():
         "attend": no_scale_attend,
         "indexer_scores": dropped_dim_scores,
         "local_blocks": local_three,
+        "page_tiers": reversed_tiers,
     }
 
 
@@ -457,6 +575,8 @@ def _pins_pass():
         lambda: test_selection_brute_force(1),
         test_indexer_scores_exact_integers,
         lambda: test_local_always_kept_and_sizes(2047),
+        test_page_gate_golden,
+        lambda: test_page_gate_brute_force(1),
     ]
     try:
         for c in checks:
