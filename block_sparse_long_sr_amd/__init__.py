@@ -55,6 +55,8 @@ class KV(ctypes.Structure):
         ("num_blocks", ctypes.c_int64),
         ("batch", ctypes.c_int32),
         ("max_blocks", ctypes.c_int32),
+        ("block_page", ctypes.c_void_p),
+        ("query_page", ctypes.c_void_p),
     ]
 
 
@@ -143,9 +145,12 @@ def make_cfg(topk_blocks: int = 16, local_blocks: int = 4, num_heads: int = 10, 
     return SparseCfg(block_size, topk_blocks, local_blocks, num_heads, head_dim, index_dim, sm_scale)
 
 
-def make_kv(k_pool, v_pool, kidx_pool, block_table, ctx_lens, num_blocks: int, batch: int, max_blocks: int) -> KV:
+def make_kv(k_pool, v_pool, kidx_pool, block_table, ctx_lens, num_blocks: int, batch: int, max_blocks: int,
+            block_page=None, query_page=None) -> KV:
+    """``block_page`` / ``query_page`` (int32 device tensors or None) turn on
+    the page-aware ranking of the selecting entry points."""
     return KV(_ptr(k_pool), _ptr(v_pool), _ptr(kidx_pool), _ptr(block_table), _ptr(ctx_lens),
-              int(num_blocks), int(batch), int(max_blocks))
+              int(num_blocks), int(batch), int(max_blocks), _ptr(block_page), _ptr(query_page))
 
 
 def indexer_score_decode(cfg: SparseCfg, kv: KV, q_idx, block_scores, stream=None) -> None:

@@ -95,6 +95,14 @@ int check_kv(const uocr_kv* kv, bool need_kidx, bool need_kv) {
   return UOCR_OK;
 }
 
+// Optional page tags (uocr_kv.block_page / query_page): both or neither.
+int check_page_gate(const uocr_kv* kv) {
+  if (kv->block_page == nullptr) return UOCR_OK;
+  REQ_PTR4(kv->block_page, "kv->block_page");
+  REQ_PTR4(kv->query_page, "kv->query_page (required with kv->block_page)");
+  return UOCR_OK;
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(UOCR_EHIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -226,6 +234,7 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
   OPT_PTR4(n_sel, "n_sel");
   REQ_PTR4(out, "out");
   OPT_PTR4(lse, "lse");
+  TRY(check_page_gate(kv));
   uocr::SelAttnArgs sa{};
   uocr::AttnArgs& a = sa.attn;
   a.k_pool = kv->k_pool;
@@ -248,6 +257,8 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
   sa.block_idx_out = block_idx;
   sa.n_sel = n_sel;
   sa.local_blocks = cfg->local_blocks;
+  sa.block_page = kv->block_page;
+  sa.query_page = kv->block_page != nullptr ? kv->query_page : nullptr;
   return hip_status(uocr::launch_select_attn(sa, static_cast<hipStream_t>(stream)), "topk_attn_decode");
 }
 
@@ -264,6 +275,7 @@ int uocr_indexer_score_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, co
   if (!aligned16(cand_ws)) return fail(UOCR_EINVAL, "cand_ws is not 16-byte aligned");
   if (cand_ws_bytes < plan.ws_bytes)
     return fail(UOCR_EWORKSPACE, "cand_ws has %zu bytes, %zu needed", cand_ws_bytes, plan.ws_bytes);
+  TRY(check_page_gate(kv));
   uocr::IndexerPrefillArgs a{};
   a.kidx_pool = kv->kidx_pool;
   a.block_table = kv->block_table;
@@ -275,6 +287,8 @@ int uocr_indexer_score_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, co
   a.max_blocks = kv->max_blocks;
   a.local_blocks = cfg->local_blocks;
   a.plan = plan;
+  a.block_page = kv->block_page;
+  a.row_page = kv->block_page != nullptr ? kv->query_page : nullptr;
   return hip_status(uocr::launch_indexer_prefill(a, static_cast<hipStream_t>(stream)), "indexer_score_prefill");
 }
 

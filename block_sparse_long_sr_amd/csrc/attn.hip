@@ -148,8 +148,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
   attend_query(a, blockIdx.x, blockIdx.y, a.block_idx + (int64_t)blockIdx.x * a.topk);
 }
 
-// Decode steps 3 and 4 in one launch: workgroup (b, h) selects the kept
-// blocks of sequence b itself (the 10 head workgroups of a sequence repeat
+// Decode steps 3 and 4 in one launch (with page tags, the page-aware
+// ranking of step 3): workgroup (b, h) selects the kept blocks of sequence b
+// itself (the 10 head workgroups of a sequence repeat
 // the same deterministic selection), keeps them in LDS and attends; the head-0
 // workgroup also writes the selection out.  This saves the separate
 // selection launch and its drain/fill gap between the scoring and attention
@@ -167,7 +168,9 @@ __global__ __launch_bounds__(kAttnThreads) void select_attn_kernel(SelAttnArgs s
   const int R = a.topk - sa.local_blocks;
   if (!select_trivial(nb, ncand, R, a.topk, s_blocks, kAttnThreads))
     select_sorted_reg<kAttnThreads, KPT>(sa.block_scores + (int64_t)b * a.max_blocks, ncand, R, sa.local_blocks,
-                                         s_blocks, sm);
+                                         s_blocks, sm,
+                                         sa.block_page != nullptr ? sa.block_page + (int64_t)b * a.max_blocks : nullptr,
+                                         sa.block_page != nullptr ? sa.query_page[b] : 0);
   __syncthreads();
   if (h == 0) {
     for (int i = threadIdx.x; i < a.topk; i += kAttnThreads) sa.block_idx_out[(int64_t)b * a.topk + i] = s_blocks[i];

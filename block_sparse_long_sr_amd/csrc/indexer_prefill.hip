@@ -58,13 +58,6 @@ typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 // s_waitcnt lgkmcnt(0) only.
 #define UOCR_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
 
-// Candidate key of a block score: the order-preserving key, at least 1, so
-// that an empty list slot (key 0) ranks below every block, NaN included.
-__device__ __forceinline__ uint32_t cand_key(float f) {
-  const uint32_t k = order_key(f);
-  return k > 1u ? k : 1u;
-}
-
 __device__ __forceinline__ float max16(const f32x16_t& v) {
   float m = fmaxf(fmaxf(v[0], v[1]), v[2]);
 #pragma unroll
@@ -97,9 +90,10 @@ __device__ __forceinline__ int simd_turn(uint32_t* counters) {
 // waits to the explicit counts below.
 template <int R>
 __device__ __forceinline__ void prefill_blocks(const IndexerPrefillArgs& a, int jb, int je, int tw, int lim,
-                                               int turn, lds_u8* __restrict__ B0, lds_u8* __restrict__ B1,
-                                               lds_u8* __restrict__ B2, lds_u8* __restrict__ B3,
-                                               lds_i32* __restrict__ tbl, const unsigned char* __restrict__ pool,
+                                               int turn, int32_t qpage, lds_u8* __restrict__ B0,
+                                               lds_u8* __restrict__ B1, lds_u8* __restrict__ B2,
+                                               lds_u8* __restrict__ B3, lds_i32* __restrict__ tbl,
+                                               lds_i32* __restrict__ tags, const unsigned char* __restrict__ pool,
                                                uint32_t (&lk)[R]) {
   const PrefillPlan& P = a.plan;
   lim = min(lim, je - 1);  // steps past the split's end keep nothing
@@ -109,7 +103,11 @@ __device__ __forceinline__ void prefill_blocks(const IndexerPrefillArgs& a, int 
   const int h = lane >> 5;
   const int n = lane & 31;
 
-  for (int i = tid; i < je - jb; i += kPfThreads) tbl[i] = a.block_table[jb + i];
+  const bool gate = a.block_page != nullptr;  // page-aware ranking
+  for (int i = tid; i < je - jb; i += kPfThreads) {
+    tbl[i] = a.block_table[jb + i];
+    if (gate) tags[i] = a.block_page[jb + i];
+  }
 
   // Resident query fragments: tile c, step s -> dims 64h + 8s .. +8 of row
   // tw + 32c + n (rows past T read row T-1 and are never kept).
@@ -186,7 +184,12 @@ __device__ __forceinline__ void prefill_blocks(const IndexerPrefillArgs& a, int 
     float b_ = fmaxf(__uint_as_float(sw_[0]), __uint_as_float(sw_[1]));                                  \
     b_ = ok_ ? b_ : __builtin_nanf("");                                                                   \
     const uint32_t idmask_ = (1u << P.idbits) - 1u;                                                      \
-    const uint32_t k_ = cand_key(b_);                                                                     \
+    uint32_t o_ = order_key(b_);                                                                          \
+    if (gate) { /* page tier in the top bit, the score's order key below it */                           \
+      const bool tier_ = tags[jj_ - jb] == qpage;                                                         \
+      o_ = tier_ ? (0x80000000u | (o_ >> 1)) : (o_ >> 1);                                                 \
+    }                                                                                                     \
+    const uint32_t k_ = o_ > 1u ? o_ : 1u; /* empty slots are 0 */                                        \
     /* NaN (key 1) stays above empty: the order bits are at least idmask + 1 */                          \
     uint32_t p_ = ((k_ > idmask_ ? k_ : idmask_ + 1u) & ~idmask_) | (idmask_ - (uint32_t)(jj_ - jb));    \
     p_ = jj_ <= lim ? p_ : 0u; /* rows past T have lim = -1 */                                            \
@@ -267,6 +270,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
   __shared__ __attribute__((aligned(16))) unsigned char tb0[kTileBytes], tb1[kTileBytes], tb2[kTileBytes],
       tb3[kTileBytes];
   __shared__ int32_t s_tbl[kMaxBps];  // pool indices of the split's blocks
+  __shared__ int32_t s_tag[kMaxBps];  // page tags of the split's blocks (page-aware ranking)
   __shared__ uint32_t s_turns[4];
 
   const PrefillPlan P = a.plan;
@@ -301,8 +305,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
 #pragma unroll
   for (int r = 0; r < R; ++r) lk[r] = 0u;
   if (jb < je) {
-    prefill_blocks<R>(a, jb, je, tw, lim, turn, (lds_u8*)tb0, (lds_u8*)tb1, (lds_u8*)tb2, (lds_u8*)tb3,
-                      (lds_i32*)s_tbl, reinterpret_cast<const unsigned char*>(a.kidx_pool), lk);
+    const int32_t qpage = (a.block_page != nullptr && row < a.T) ? a.row_page[row] : 0;
+    prefill_blocks<R>(a, jb, je, tw, lim, turn, qpage, (lds_u8*)tb0, (lds_u8*)tb1, (lds_u8*)tb2, (lds_u8*)tb3,
+                      (lds_i32*)s_tbl, (lds_i32*)s_tag, reinterpret_cast<const unsigned char*>(a.kidx_pool), lk);
   }
   if (row < a.T) {
     uint32_t* dst = a.cand_keys + ((size_t)row * P.nsplit + split) * R;

@@ -65,6 +65,8 @@ struct SelAttnArgs {
   int32_t* block_idx_out;      // [B][topk], written
   int32_t* n_sel;              // [B] or null
   int32_t local_blocks;
+  const int32_t* block_page;   // [B][max_blocks] page tags or null (plain ranking)
+  const int32_t* query_page;   // [B] query pages (with block_page)
 };
 hipError_t launch_select_attn(const SelAttnArgs& a, hipStream_t stream);
 
@@ -90,6 +92,8 @@ struct IndexerPrefillArgs {
   int32_t max_blocks;
   int32_t local_blocks;
   PrefillPlan plan;
+  const int32_t* block_page;   // row of sequence 0: page tags, or null (plain ranking)
+  const int32_t* row_page;     // [T] page of each row (with block_page)
 };
 hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t stream);
 

@@ -126,9 +126,14 @@ struct SelectSmem {
 // Non-trivial case (ncand > R >= 1): writes the R remote ids ascending, then
 // the local window, into out[0 .. R + local_blocks).  `out` may point to
 // global or LDS memory.  Every thread of the NT-thread workgroup calls it.
+// With page tags (`tags` not null; news.rkmt.cn/news/25027 Sec. 5, the
+// page-aware candidate constraint) a candidate's tier -- 1 when its tag
+// equals `qpage` -- takes the top bit of its ranking key and the score's
+// order key the 31 bits below, so the query's page's blocks rank first.
 template <int NT, int KPT>
 __device__ __forceinline__ void select_sorted_reg(const float* sc, int ncand, int R, int local_blocks, int32_t* out,
-                                                  SelectSmem<NT>& sm) {
+                                                  SelectSmem<NT>& sm, const int32_t* tags = nullptr,
+                                                  int32_t qpage = 0) {
   constexpr int kCap = SelectSmem<NT>::kCap;
   uint32_t* hist = sm.hist;
   uint32_t* scan_scratch = sm.scan_scratch;
@@ -148,6 +153,14 @@ __device__ __forceinline__ void select_sorted_reg(const float* sc, int ncand, in
   }
 #pragma unroll
   for (int i = 0; i < KPT; ++i) key[i] = (tid + i * NT < ncand) ? order_key(__uint_as_float(key[i])) : 0u;
+  if (tags != nullptr) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int j = tid + i * NT;
+      const bool tier = tags[j < ncand ? j : ncand - 1] == qpage;
+      key[i] = tier ? (0x80000000u | (key[i] >> 1)) : (key[i] >> 1);
+    }
+  }
 
   // ---- pass A: top byte, one wave sum per distinct digit -------------------
   if (tid < 256) hist[tid] = 0;

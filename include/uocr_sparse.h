@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define UOCR_ABI_VERSION 1
+#define UOCR_ABI_VERSION 2
 
 /* Status codes. */
 enum {
@@ -94,6 +94,27 @@ typedef struct uocr_sparse_cfg {
  *   ctx_lens       : [batch] int32, tokens in the cache per sequence
  * A block x head of K or V is one contiguous 8 KB row group, an indexer block
  * one contiguous 8 KB tile, so every gather is fully coalesced.
+ *
+ * Page-aware candidates (optional; news.rkmt.cn/news/25027 Sec. 5, the
+ * page-aware candidate constraint: the query's own page's image blocks, the
+ * local window and a global fallback; leheavengame.com OCR 2 release article
+ * Sec. 2 route A, Page Gate).  When block_page is not NULL the remote
+ * candidates of a query are ranked by tier first -- tier 1 for blocks tagged
+ * with the query's page, tier 0 for all others -- then by score descending
+ * and lower block id; the local window is unchanged.  So the query's page's
+ * image blocks are kept first and the remaining slots fall back to the best
+ * other blocks.
+ *   block_page : [batch][max_blocks] int32, the page whose image tokens the
+ *                logical block holds, or -1 for blocks holding none
+ *   query_page : decode: [batch] int32, the page of each sequence's query;
+ *                prefill: [T] int32, the page of each chunk row.  Required
+ *                (UOCR_EINVAL otherwise) when block_page is set.
+ * Both NULL: plain ranking.  With tiers, a score keeps one bit less of
+ * precision in the ranking key (decode: 2^-22 relative; prefill: see
+ * uocr_indexer_score_prefill).  Honoured by uocr_topk_attn_decode and
+ * uocr_indexer_score_prefill (whose lists uocr_block_topk_prefill merges);
+ * uocr_block_topk_decode, which takes no kv, always ranks plainly, and the
+ * scoring and attention entries do not use them.
  */
 typedef struct uocr_kv {
   const uint16_t* k_pool;
@@ -104,6 +125,8 @@ typedef struct uocr_kv {
   int64_t num_blocks;  /* pool blocks P (>= 1)                               */
   int32_t batch;       /* sequences B (>= 0)                                 */
   int32_t max_blocks;  /* block-table row length (>= 1, <= 1,048,576)        */
+  const int32_t* block_page; /* optional page tags, see above (NULL: off)   */
+  const int32_t* query_page; /* optional query pages, see above              */
 } uocr_kv;
 
 /* ---------------------------------------------------------------- decode */
@@ -190,8 +213,14 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
  *   q_idx   : [T][Di] bf16
  *   cand_ws : workspace of uocr_workspace_size(cfg, UOCR_OP_INDEXER_PREFILL,
  *             T, max_blocks) bytes
- * Requires 0 <= q_start, T >= 0, q_start + T <= 32 * max_blocks,
- * topk_blocks - local_blocks <= 16.
+ * Ranking precision: a list entry keeps a block score's order bits above an
+ * in-split block index of idbits = ceil(log2(blocks per split)) <= 9 bits, so
+ * rows are ranked on scores truncated to 2^-(23-idbits) relative (2^-17 at
+ * 128K context, 2^-14 at worst; one bit less with page tiers), equal
+ * truncated scores going to the lower block id.
+ * Requires 0 <= q_start, T >= 0, q_start + T <= 32 * max_blocks <= 32 * 32768,
+ * topk_blocks - local_blocks <= 16 (UOCR_EUNSUPPORTED beyond).  With page
+ * tags, kv->query_page holds one page per row ([T]).
  */
 int uocr_indexer_score_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q_idx,
                                int32_t q_start, int32_t T, void* cand_ws, size_t cand_ws_bytes, void* stream);

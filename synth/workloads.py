@@ -289,6 +289,27 @@ def config4(batch: int = 64, min_pages: int = 5, max_pages: int = 65) -> Workloa
     return wl
 
 
+def page_tags(max_blocks: int, page_tokens: int = PAGE_TOKENS, image_tokens: int = PAGE_IMAGE) -> np.ndarray:
+    """Page tag of each logical block when a document is laid out as pages of
+    ``image_tokens`` image tokens followed by text, ``page_tokens`` tokens per
+    page: the page whose image tokens the block holds, or -1 for a block with
+    none.  This is input metadata for the page-aware ranking (a block never
+    holds image tokens of two pages while a page has more than 32 text
+    tokens)."""
+    tags = np.full(max_blocks, -1, np.int32)
+    for j in range(max_blocks):
+        lo, hi = j * BLOCK, j * BLOCK + BLOCK - 1
+        for pg in range(lo // page_tokens, hi // page_tokens + 1):
+            if lo < pg * page_tokens + image_tokens and hi >= pg * page_tokens:
+                tags[j] = pg
+    return tags
+
+
+def page_of(position: int, page_tokens: int = PAGE_TOKENS) -> int:
+    """Page holding token ``position`` (the query's page)."""
+    return int(position) // page_tokens
+
+
 def config5(rows: int = 2048, S: int = 131072) -> Workload:
     """Chunked prefill: 2048 new rows at offset S-2048 of an S-token context."""
     return Workload(name=f"chunked prefill T={rows} at {S - rows} of S={S}", seed=0x5EED0005, batch=1,

@@ -10,7 +10,8 @@ Tolerances (written here, used by every parity test):
   Sec. 3.1), and the block max is 1-Lipschitz.
 * selection: equal sets, except blocks whose oracle score lies within 1e-4
   relative of the oracle's cutoff score (the ambiguity band), where either
-  choice is accepted as long as both sets have the same size.
+  choice is accepted as long as both sets have the same size.  With page
+  tiers the band holds only blocks of the cutoff block's tier.
 * attention (given the same index set): max-abs <= 2e-3 and relative L2 <=
   1e-3 per query; lse within 1e-4 absolute.
 """
@@ -154,7 +155,10 @@ def check_selection(gpu_idx_row: np.ndarray, ref: Dict, topk: int):
     if ref["cutoff"] is not None:
         c = ref["cutoff"]
         bs = ref["block_scores"].astype(np.float64)
-        band = set(np.nonzero(np.abs(bs - c) <= BAND * abs(c))[0].tolist())
+        near = np.abs(bs - c) <= BAND * abs(c)
+        if ref.get("tiers") is not None:   # page-aware: only the cutoff's own tier is ambiguous
+            near &= ref["tiers"] == ref["cutoff_tier"]
+        band = set(np.nonzero(near)[0].tolist())
     assert len(got) == len(want), f"size {len(got)} != {len(want)}"
     assert set(got) - band == set(want) - band, f"gpu {got} oracle {want} band {sorted(band)}"
     for j in ref["local"]:

@@ -41,7 +41,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["uocr_indexer_score_decode", "uocr_block_topk_decode", "uocr_sparse_attn_decode",
-              "uocr_indexer_score_prefill", "uocr_block_topk_prefill", "uocr_sparse_attn_prefill",
+              "uocr_topk_attn_decode", "uocr_indexer_score_prefill", "uocr_block_topk_prefill", "uocr_sparse_attn_prefill",
               "uocr_workspace_size", "uocr_status_string", "uocr_last_error", "uocr_abi_version"]:
         assert n in names
 
@@ -52,10 +52,28 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), f"{n} not exported"
 
 
-def test_struct_layouts_match_header(U):
-    assert ctypes.sizeof(U.SparseCfg) == 28
-    assert ctypes.sizeof(U.KV) == 5 * 8 + 8 + 4 + 4
-    assert U.abi_version() == 1
+def test_struct_layouts_match_header(U, tmp_path):
+    """The binding's ctypes mirrors have the sizes and field offsets that a C
+    compiler gives the header's structs."""
+    import subprocess
+    fields = {"uocr_sparse_cfg": [f for f, _ in U.SparseCfg._fields_], "uocr_kv": [f for f, _ in U.KV._fields_]}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "uocr_sparse.h"', "int main(void) {"]
+    for st, fs in fields.items():
+        lines.append(f'  printf("{st} %zu\\n", sizeof({st}));')
+        for f in fs:
+            lines.append(f'  printf("{st}.{f} %zu\\n", offsetof({st}, {f}));')
+    lines += ['  printf("abi %d\\n", UOCR_ABI_VERSION);', "  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                 text=True).stdout.splitlines())
+    for st, cls in (("uocr_sparse_cfg", U.SparseCfg), ("uocr_kv", U.KV)):
+        assert int(got[st]) == ctypes.sizeof(cls)
+        for f in fields[st]:
+            assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, f
+    assert int(got["abi"]) == U.abi_version() == 2
 
 
 def test_status_strings(U):
@@ -133,6 +151,26 @@ def test_fused_decode_argument_checks(U):
         U.topk_attn_decode(cfg, _kv(U), FAKE, FAKE, FAKE, None, stream=0)
     assert e.value.status == 1 and "out" in U.last_error()
     assert U.workspace_size(cfg, 2, 16, 4096) == 0
+
+
+def test_page_tags_need_query_pages(U):
+    cfg = U.make_cfg()
+    kv = _kv(U)
+    kv.block_page = FAKE
+    with pytest.raises(U.UocrError) as e:      # tags without query pages
+        U.topk_attn_decode(cfg, kv, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == 1 and "query_page" in U.last_error()
+    kv.query_page = FAKE + 2                    # misaligned int32 array
+    with pytest.raises(U.UocrError) as e:
+        U.topk_attn_decode(cfg, kv, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == 1 and "query_page" in U.last_error()
+    kv1 = _kv(U, batch=1, max_blocks=64)
+    kv1.block_page = FAKE + 1
+    kv1.query_page = FAKE
+    ws = U.workspace_size(cfg, U.OP_INDEXER_PREFILL, 100, 64)
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_prefill(cfg, kv1, FAKE, 1900, 100, (FAKE, ws), stream=0)
+    assert e.value.status == 1 and "block_page" in U.last_error()
 
 
 def test_empty_batch_is_a_no_op(U):
