@@ -191,6 +191,83 @@ def run_prefill(U, SD, W, torch, iters=5):
     return res
 
 
+def run_page_gate(U, SD, W, torch, reps=20):
+    """Page-aware ranking on the multi-page workloads: the ragged decode batch
+    (64 documents of 400 image + 600 text tokens per page, query on the last
+    page) and the 128K prefill chunk laid out in the same pages; each timed
+    with and without the page tags (one event pair around back-to-back
+    repetitions)."""
+    import numpy as np
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    res = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        for _ in range(reps):
+            fn()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return a_.elapsed_time(b_) / reps
+
+    wl = W.config4()
+    dev = SD.generate(wl)
+    cfg = U.make_cfg()
+    B, M, H = wl.batch, wl.max_blocks, 10
+    tags = torch.from_numpy(np.tile(W.page_tags(M), (B, 1)).astype(np.int32)).cuda()
+    qp = torch.from_numpy(np.array([W.page_of(L - 1) for L in wl.ctx_lens], np.int32)).cuda()
+    kv_plain = dev.kv(0)
+    kv_gate = U.make_kv(dev.k[0], dev.v[0], dev.kidx[0], dev.block_table, dev.ctx_lens, wl.pool_blocks, B, M,
+                        tags, qp)
+    scores = torch.empty((B, M), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, 16), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+
+    def step(kv):
+        U.indexer_score_decode(cfg, kv, dev.q_idx[0], scores, stream=sh)
+        U.topk_attn_decode(cfg, kv, dev.q[0], scores, idx, out, lse, stream=sh)
+
+    t_plain = timed(lambda: step(kv_plain))
+    t_gate = timed(lambda: step(kv_gate))
+    idx_b, topk_b, attn_b = decode_bytes(wl)
+    step_bytes = idx_b + topk_b + attn_b
+    res["decode"] = {"workload": wl.name, "queries": B, "algorithmic_bytes": step_bytes,
+                     "us": {"plain": t_plain * 1e3, "page_aware": t_gate * 1e3},
+                     "query_heads_per_s": {"plain": B * H / (t_plain * 1e-3), "page_aware": B * H / (t_gate * 1e-3)},
+                     "hbm_GBps_page_aware": step_bytes / (t_gate * 1e-3) / 1e9}
+    del dev, scores, out
+    torch.cuda.empty_cache()
+
+    wl = W.config5()
+    dev = SD.generate(wl)
+    T, M = wl.rows, wl.max_blocks
+    tags = torch.from_numpy(W.page_tags(M)[None, :].astype(np.int32)).cuda()
+    rp = torch.from_numpy(np.array([W.page_of(wl.q_start + t) for t in range(T)], np.int32)).cuda()
+    kv_plain = dev.kv(0)
+    kv_gate = U.make_kv(dev.k[0], dev.v[0], dev.kidx[0], dev.block_table, dev.ctx_lens, wl.pool_blocks, 1, M,
+                        tags, rp)
+    ws_bytes = U.workspace_size(cfg, U.OP_INDEXER_PREFILL, T, M)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    wsarg = (ws.data_ptr(), ws_bytes)
+    bidx = torch.empty((T, 16), dtype=torch.int32, device="cuda")
+
+    def score(kv):
+        U.indexer_score_prefill(cfg, kv, dev.q_idx, wl.q_start, T, wsarg, stream=sh)
+        U.block_topk_prefill(cfg, wsarg, wl.q_start, T, M, bidx, stream=sh)
+
+    res["prefill_scoring_and_merge"] = {"workload": wl.name + ", pages of 400 image + 600 text tokens",
+                                        "us": {"plain": timed(lambda: score(kv_plain)) * 1e3,
+                                               "page_aware": timed(lambda: score(kv_gate)) * 1e3}}
+    del dev, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +283,7 @@ def main():
                     help="layers of the workload the CPU oracle is timed on (x16 queries)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-page-gate", action="store_true", help="skip the page-aware ranking measurement")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the chunked-prefill case (profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -415,6 +493,14 @@ def main():
         log(f"prefill scoring {pf['ms']['scoring_back_to_back'] * 1e3:.1f} us back to back "
             f"({pf['scoring_roofline']['achieved']:.0f} TFLOP/s), {pf['ms']['scoring'] * 1e3:.1f} us in the "
             f"chunk step; merge {pf['ms']['merge'] * 1e3:.1f} us; attention {pf['ms']['attention'] * 1e3:.1f} us")
+
+    if not args.no_page_gate:
+        log("page-aware ranking: ragged multi-page decode and the 128K prefill chunk, with and without page tags")
+        result["page_gate"] = run_page_gate(U, SD, W, torch)
+        pg = result["page_gate"]
+        log(f"page-aware decode {pg['decode']['us']['page_aware']:.1f} us (plain {pg['decode']['us']['plain']:.1f} us); "
+            f"prefill scoring+merge {pg['prefill_scoring_and_merge']['us']['page_aware']:.1f} us "
+            f"(plain {pg['prefill_scoring_and_merge']['us']['plain']:.1f} us)")
 
     print(json.dumps(result), flush=True)
 
