@@ -284,6 +284,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-page-gate", action="store_true", help="skip the page-aware ranking measurement")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense full-context comparator")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the chunked-prefill case (profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -484,6 +485,32 @@ def main():
         }
         log(f"cpu oracle {nq * H / secs:.1f} query-heads/s")
 
+    if not args.no_dense:
+        # Dense full-context attention of the same step (the comparator for the
+        # pages' per-step speed claim against full attention): every query
+        # attends to all 131072 tokens of its sequence in each of the 12 layers.
+        wsb = U.workspace_size(cfg, U.OP_DENSE_ATTN_DECODE, B, M)
+        dws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        dwarg = (dws.data_ptr(), wsb)
+        U.dense_attn_decode(cfg, kvs[0], dev.q[0], out[0], lse[0], ws=dwarg, stream=sh)
+        torch.cuda.synchronize()
+        reps = 2
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        for _ in range(reps):
+            for l in range(L):
+                U.dense_attn_decode(cfg, kvs[l], dev.q[l], out[l], lse[l], ws=dwarg, stream=sh)
+        b_.record(stream)
+        torch.cuda.synchronize()
+        ms_dense = a_.elapsed_time(b_) / reps
+        dense_bytes = L * sum(int(x) * 10 * 128 * 2 * 2 for x in wl.ctx_lens)
+        result["dense_comparator"] = {
+            "what": "full-context decode attention (all tokens, 10 heads) for the same 12 layers x 16 sequences",
+            "ms_per_step": ms_dense, "sparse_ms_per_step": ms_step, "speedup_sparse_over_dense": ms_dense / ms_step,
+            "kv_bytes_per_step": dense_bytes, "achieved_GBps": dense_bytes / (ms_dense * 1e-3) / 1e9}
+        log(f"dense full-context attention step {ms_dense:.2f} ms ({dense_bytes / (ms_dense * 1e-3) / 1e9:.0f} GB/s): "
+            f"sparse step is {ms_dense / ms_step:.1f}x faster")
+        del dws
     del dev, scores, out
     torch.cuda.empty_cache()
     if not args.no_prefill:

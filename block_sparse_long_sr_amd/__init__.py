@@ -21,7 +21,7 @@ __all__ = [
     "indexer_score_prefill", "block_topk_prefill", "sparse_attn_prefill",
     "workspace_size", "status_string", "last_error", "abi_version",
     "OP_INDEXER_DECODE", "OP_TOPK_DECODE", "OP_ATTN_DECODE",
-    "OP_INDEXER_PREFILL", "OP_TOPK_PREFILL", "OP_ATTN_PREFILL",
+    "OP_INDEXER_PREFILL", "OP_TOPK_PREFILL", "OP_ATTN_PREFILL", "OP_DENSE_ATTN_DECODE", "dense_attn_decode",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,6 +29,7 @@ lib_path = os.path.join(_HERE, "libuocr_sparse.so")
 
 OP_INDEXER_DECODE, OP_TOPK_DECODE, OP_ATTN_DECODE = 0, 1, 2
 OP_INDEXER_PREFILL, OP_TOPK_PREFILL, OP_ATTN_PREFILL = 3, 4, 5
+OP_DENSE_ATTN_DECODE = 6
 
 
 class SparseCfg(ctypes.Structure):
@@ -85,6 +86,7 @@ _SIGS = {
     "uocr_block_topk_decode": ([_CFG, _P, _P, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "uocr_sparse_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "uocr_topk_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "uocr_dense_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "uocr_indexer_score_prefill": ([_CFG, _KV, _P, _I32, _I32, _P, _SZ, _P], ctypes.c_int),
     "uocr_block_topk_prefill": ([_CFG, _P, _SZ, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "uocr_sparse_attn_prefill": ([_CFG, _KV, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
@@ -174,6 +176,13 @@ def topk_attn_decode(cfg: SparseCfg, kv: KV, q, block_scores, block_idx, out, ls
     _check(_lib.uocr_topk_attn_decode(ctypes.byref(cfg), ctypes.byref(kv), _ptr(q), _ptr(block_scores),
                                       _ptr(block_idx), _ptr(n_sel), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws),
                                       _stream(stream)), "topk_attn_decode")
+
+
+def dense_attn_decode(cfg: SparseCfg, kv: KV, q, out, lse=None, ws=None, stream=None) -> None:
+    """Full-context attention of each sequence's query (the dense comparator);
+    ``ws`` as for the other entries: a tensor or (pointer, bytes)."""
+    _check(_lib.uocr_dense_attn_decode(ctypes.byref(cfg), ctypes.byref(kv), _ptr(q), _ptr(out), _ptr(lse), _ptr(ws),
+                                       _nbytes(ws), _stream(stream)), "dense_attn_decode")
 
 
 def indexer_score_prefill(cfg: SparseCfg, kv: KV, q_idx, q_start: int, T: int, cand_ws, stream=None) -> None:

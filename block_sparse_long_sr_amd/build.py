@@ -27,9 +27,8 @@ DEVICE_FLAGS = [
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC"]
 
-SOURCES = ["api.cpp", "indexer_decode.hip", "topk_decode.hip", "attn.hip", "indexer_prefill.hip"]
-# MFMA results in ordinary VGPRs: the prefill epilogue reads every accumulator
-# with vector ALU instructions, which AGPRs would first have to be copied out of.
+SOURCES = ["api.cpp", "indexer_decode.hip", "topk_decode.hip", "attn.hip", "indexer_prefill.hip", "dense_attn.hip"]
+# Extra hipcc flags per source file (none at present).
 PER_FILE_FLAGS = {}
 
 

@@ -262,6 +262,37 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
   return hip_status(uocr::launch_select_attn(sa, static_cast<hipStream_t>(stream)), "topk_attn_decode");
 }
 
+int uocr_dense_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q, float* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_cfg(cfg));
+  TRY(check_kv(kv, false, true));
+  if (kv->batch == 0) return ok();
+  REQ_PTR4(kv->ctx_lens, "kv->ctx_lens");
+  REQ_PTR16(q, "q");
+  REQ_PTR4(out, "out");
+  OPT_PTR4(lse, "lse");
+  const uocr::DensePlan plan = uocr::dense_plan(kv->batch, cfg->num_heads, kv->max_blocks);
+  if (ws == nullptr) return fail(UOCR_EWORKSPACE, "ws is NULL (%zu bytes needed)", plan.ws_bytes);
+  if (!aligned16(ws)) return fail(UOCR_EINVAL, "ws is not 16-byte aligned");
+  if (ws_bytes < plan.ws_bytes) return fail(UOCR_EWORKSPACE, "ws has %zu bytes, %zu needed", ws_bytes, plan.ws_bytes);
+  uocr::DenseArgs a{};
+  a.k_pool = kv->k_pool;
+  a.v_pool = kv->v_pool;
+  a.block_table = kv->block_table;
+  a.ctx_lens = kv->ctx_lens;
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.ws = static_cast<float*>(ws);
+  a.num_blocks = kv->num_blocks;
+  a.batch = kv->batch;
+  a.heads = cfg->num_heads;
+  a.max_blocks = kv->max_blocks;
+  a.scale_log2 = cfg->sm_scale * 1.44269504088896340736f;
+  a.plan = plan;
+  return hip_status(uocr::launch_dense_attn(a, static_cast<hipStream_t>(stream)), "dense_attn_decode");
+}
+
 int uocr_indexer_score_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q_idx,
                                int32_t q_start, int32_t T, void* cand_ws, size_t cand_ws_bytes, void* stream) {
   TRY(check_cfg(cfg));
@@ -338,6 +369,8 @@ int uocr_sparse_attn_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, cons
 size_t uocr_workspace_size(const uocr_sparse_cfg* cfg, int32_t op, int32_t rows, int32_t max_blocks) {
   if (check_cfg(cfg) != UOCR_OK || rows < 0 || max_blocks < 1 || max_blocks > kMaxBlocks) return 0;
   switch (op) {
+    case UOCR_OP_DENSE_ATTN_DECODE:
+      return uocr::dense_plan(rows, cfg->num_heads, max_blocks).ws_bytes;
     case UOCR_OP_INDEXER_PREFILL:
     case UOCR_OP_TOPK_PREFILL:
       if (cfg->topk_blocks - cfg->local_blocks > kMaxRemotePrefill || max_blocks > kMaxBlocksPrefill) return 0;

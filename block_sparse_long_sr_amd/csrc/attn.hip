@@ -7,12 +7,10 @@
 // One 1024-thread workgroup per (query, head): the kept blocks are split over
 // its 16 waves (split-K; at 16 kept blocks every block's K and V loads are in
 // flight at once), each wave keeps an online-softmax state (running
-// max, sum, 128-dim accumulator) and the waves' states are merged through LDS
-// at the end.  A wave reads a block's 8 KB K tile and 8 KB V tile with
-// contiguous 1 KB loads: lane l holds dims 8*(l%16)..+8 of keys 4k + l/16
-// (k = 0..7), which are exactly the keys whose probabilities it needs for its
-// V slice, so scores never leave the lane's DPP row.  Arithmetic is fp32
-// with exp2 on log2e-scaled logits; the output is fp32.
+// max, sum, 128-dim accumulator; attend_block in attn_common.h) and the
+// waves' states are merged through LDS at the end.  Arithmetic is fp32 with
+// exp2 on log2e-scaled logits; the output is fp32.
+#include "attn_common.h"
 #include "device_common.h"
 #include "kernels.h"
 #include "select_common.h"
@@ -33,7 +31,6 @@ __device__ __forceinline__ void attend_query(const AttnArgs& a, int qi, int h, c
 
   const int lane = lane_id();
   const int wave = wave_id();
-  const int g = lane >> 4;        // key row group within a 4-key slab
   const int c8 = (lane & 15) * 8; // first dim of the lane's slice
 
   int seq, p;
@@ -60,58 +57,10 @@ __device__ __forceinline__ void attend_query(const AttnArgs& a, int qi, int h, c
     const int pb = __builtin_amdgcn_readfirstlane(table[j]);
     if (pb < 0 || (int64_t)pb >= a.num_blocks) continue;
     const int64_t tile = ((int64_t)pb * a.heads + h) * (kBlock * kDim);
-    const uint4* kt = reinterpret_cast<const uint4*>(a.k_pool + tile);
-    const uint4* vt = reinterpret_cast<const uint4*>(a.v_pool + tile);
-    uint4 kv[8], vv[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) kv[k] = kt[k * kWave + lane];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) vv[k] = vt[k * kWave + lane];
-
-    const bool full = j * kBlock + (kBlock - 1) <= p;
-    float s[8];
-    float bm = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float z = row16_sum(dot8_bf16(kv[k], qv)) * a.scale_log2;
-      if (!full && j * kBlock + 4 * k + g > p) z = -INFINITY;
-      s[k] = z;
-      bm = fmaxf(bm, z);
-    }
-    bm = fmaxf(bm, shfl_xor_f32(bm, 16));
-    bm = fmaxf(bm, shfl_xor_f32(bm, 32));
-    const float m_new = fmaxf(m, bm);
-    const float alpha = exp2f(m - m_new);
-    l *= alpha;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] *= alpha;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const bool valid = full || (j * kBlock + 4 * k + g <= p);
-      const float pk = valid ? exp2f(s[k] - m_new) : 0.0f;
-      l += pk;
-      if (valid) {
-        o[0] += pk * bf16_lo(vv[k].x);
-        o[1] += pk * bf16_hi(vv[k].x);
-        o[2] += pk * bf16_lo(vv[k].y);
-        o[3] += pk * bf16_hi(vv[k].y);
-        o[4] += pk * bf16_lo(vv[k].z);
-        o[5] += pk * bf16_hi(vv[k].z);
-        o[6] += pk * bf16_lo(vv[k].w);
-        o[7] += pk * bf16_hi(vv[k].w);
-      }
-    }
-    m = m_new;
+    attend_block(a.k_pool + tile, a.v_pool + tile, j, p, qv, a.scale_log2, m, l, o);
   }
 
-  // Sum the four key groups of the wave (lanes l, l^16, l^32, l^48).
-  l += shfl_xor_f32(l, 16);
-  l += shfl_xor_f32(l, 32);
-#pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    o[d] += shfl_xor_f32(o[d], 16);
-    o[d] += shfl_xor_f32(o[d], 32);
-  }
+  reduce_key_groups(l, o);
   if (lane == 0) {
     s_m[wave] = m;
     s_l[wave] = l;

@@ -70,6 +70,32 @@ struct SelAttnArgs {
 };
 hipError_t launch_select_attn(const SelAttnArgs& a, hipStream_t stream);
 
+// Dense full-context decode attention (comparator): split-K partials in a
+// workspace, then a merge.
+struct DensePlan {
+  int32_t nsplit;   // block-range splits per (sequence, head)
+  int32_t bps;      // blocks per split
+  size_t ws_bytes;  // batch * heads * nsplit * (128 + 2) floats
+};
+DensePlan dense_plan(int32_t batch, int32_t heads, int32_t max_blocks);
+struct DenseArgs {
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  const uint16_t* q;   // [B][H][D]
+  float* out;          // [B][H][D]
+  float* lse;          // [B][H] or null
+  float* ws;           // partials
+  int64_t num_blocks;
+  int32_t batch;
+  int32_t heads;
+  int32_t max_blocks;
+  float scale_log2;
+  DensePlan plan;
+};
+hipError_t launch_dense_attn(const DenseArgs& a, hipStream_t stream);
+
 // Chunked-prefill scoring: partition of the context into splits.
 struct PrefillPlan {
   int32_t n_tiles;   // ceil(T / 256) row tiles

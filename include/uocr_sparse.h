@@ -64,7 +64,8 @@ enum {
   UOCR_OP_ATTN_DECODE = 2,
   UOCR_OP_INDEXER_PREFILL = 3,
   UOCR_OP_TOPK_PREFILL = 4,
-  UOCR_OP_ATTN_PREFILL = 5
+  UOCR_OP_ATTN_PREFILL = 5,
+  UOCR_OP_DENSE_ATTN_DECODE = 6
 };
 
 /*
@@ -198,6 +199,22 @@ int uocr_sparse_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const
 int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q,
                           const float* block_scores, int32_t* block_idx, int32_t* n_sel, float* out, float* lse,
                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dense full-context decode attention, the comparator for the pages'
+ * per-step speed claim against full attention (leheavengame.com OCR 2
+ * release article, Sec. 1): per head h, softmax over ALL tokens 0..p of the
+ * sequence (p = ctx_len-1) of sm_scale * q_h . k_h, times V -- step 4
+ * without steps 2-3.  Same caches and conventions as uocr_sparse_attn_decode.
+ *   q      : [batch][H][D] bf16
+ *   out    : [batch][H][D] float32, written (0 for an empty context)
+ *   lse    : [batch][H] float32 or NULL (-inf for an empty context)
+ *   ws     : workspace of uocr_workspace_size(cfg, UOCR_OP_DENSE_ATTN_DECODE,
+ *            batch, max_blocks) bytes (split-K partials), 16-byte aligned;
+ *            UOCR_EWORKSPACE if missing or smaller
+ */
+int uocr_dense_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q, float* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------- chunked prefill */
 

@@ -41,7 +41,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["uocr_indexer_score_decode", "uocr_block_topk_decode", "uocr_sparse_attn_decode",
-              "uocr_topk_attn_decode", "uocr_indexer_score_prefill", "uocr_block_topk_prefill", "uocr_sparse_attn_prefill",
+              "uocr_topk_attn_decode", "uocr_dense_attn_decode", "uocr_indexer_score_prefill", "uocr_block_topk_prefill", "uocr_sparse_attn_prefill",
               "uocr_workspace_size", "uocr_status_string", "uocr_last_error", "uocr_abi_version"]:
         assert n in names
 
@@ -151,6 +151,23 @@ def test_fused_decode_argument_checks(U):
         U.topk_attn_decode(cfg, _kv(U), FAKE, FAKE, FAKE, None, stream=0)
     assert e.value.status == 1 and "out" in U.last_error()
     assert U.workspace_size(cfg, 2, 16, 4096) == 0
+
+
+def test_dense_decode_argument_checks(U):
+    cfg = U.make_cfg()
+    need = U.workspace_size(cfg, U.OP_DENSE_ATTN_DECODE, 16, 4096)
+    assert need > 0 and need % (130 * 4) == 0 and need // (130 * 4) % (16 * 10) == 0
+    with pytest.raises(U.UocrError) as e:
+        U.dense_attn_decode(cfg, _kv(U), FAKE, FAKE, stream=0)        # no workspace
+    assert e.value.status == 3
+    small = U.workspace_size(cfg, U.OP_DENSE_ATTN_DECODE, 2, 8)
+    with pytest.raises(U.UocrError) as e:
+        U.dense_attn_decode(cfg, _kv(U), FAKE, FAKE, ws=(FAKE, small - 4), stream=0)
+    assert e.value.status == 3
+    with pytest.raises(U.UocrError) as e:
+        U.dense_attn_decode(cfg, _kv(U, v_pool=None), FAKE, FAKE, ws=(FAKE, small), stream=0)
+    assert e.value.status == 1 and "v_pool" in U.last_error()
+    U.dense_attn_decode(cfg, _kv(U, batch=0), None, None, stream=0)   # empty batch: nothing to do
 
 
 def test_page_tags_need_query_pages(U):
