@@ -21,6 +21,10 @@ Sources (cited by short name in the docstrings):
            1.77 GB), Sec. 2 route A (Page Gate, Token Sieve, Local Window)
            and Sec. 3 (the chunked-prefill [tokens, context/32] temporary).
 
+Modules: ``sr_swa`` (steps 1-4 of the attention, the page-aware ranking)
+and ``page2d`` (the page2d rotary encoding and the cache write, [rkmt]
+Sec. 4).
+
 Where the pages leave a step open, the reading taken is stated at the
 function that implements it.
 
@@ -45,4 +49,12 @@ from .sr_swa import (  # noqa: F401
     decode_query_fetch,
     prefill_rows,
     prefill_rows_fetch,
+)
+from .page2d import (  # noqa: F401
+    page2d_inv_freq,
+    page2d_angles,
+    rope_page2d_f64,
+    rope_page2d,
+    bf16_bits_nearest,
+    cache_write,
 )
