@@ -268,6 +268,56 @@ def run_page_gate(U, SD, W, torch, reps=20):
     return res
 
 
+def run_rope(U, torch, reps=20):
+    """page2d cache write + query rotation: one decode layer of 16 sequences
+    (one new token each) and one 2048-token prefill chunk, into block-major
+    pools of 128K-token sequences; one event pair around back-to-back calls."""
+    import numpy as np
+
+    H, D, M = 10, 128, 4096
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    cfg = U.make_cfg()
+    g = np.random.default_rng(7)
+    res = {}
+    for name, B, n in (("decode: 16 sequences x 1 new token", 16, 16), ("prefill: 2048 new tokens", 1, 2048)):
+        P = B * M
+        kp = torch.zeros((P, H, 32, D), dtype=torch.int16, device="cuda")
+        vp = torch.zeros_like(kp)
+        ip = torch.zeros((P, 32, D), dtype=torch.int16, device="cuda")
+        table = torch.from_numpy(g.permutation(P).reshape(B, M).astype(np.int32)).cuda()
+        ctx = torch.full((B,), M * 32, dtype=torch.int32, device="cuda")
+        kv = U.make_kv(kp, vp, ip, table, ctx, P, B, M)
+        seq = torch.from_numpy((np.arange(n) % B).astype(np.int32)).cuda()
+        pos = torch.from_numpy((M * 32 - n // B + np.arange(n) // B).astype(np.int32)).cuda()
+        tok = torch.from_numpy((np.arange(n) % 1000).astype(np.int32)).cuda()
+        page = torch.from_numpy((np.arange(n) // 1000).astype(np.int32)).cuda()
+        kn = torch.randn((n, H, D), device="cuda").to(torch.bfloat16).view(torch.int16)
+        vn = torch.randn((n, H, D), device="cuda").to(torch.bfloat16).view(torch.int16)
+        ixn = torch.randn((n, D), device="cuda").to(torch.bfloat16).view(torch.int16)
+        q = torch.randn((n, H, D), device="cuda").to(torch.bfloat16).view(torch.int16)
+        qi = torch.randn((n, D), device="cuda").to(torch.bfloat16).view(torch.int16)
+
+        def call():
+            U.rope_cache_write(cfg, kv, n, seq, pos, tok, page, kn, vn, ixn, stream=sh)
+            U.rope_queries(cfg, n, tok, page, q=q, q_idx=qi, stream=sh)
+
+        call()
+        torch.cuda.synchronize()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        for _ in range(reps):
+            call()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        us = a_.elapsed_time(b_) / reps * 1e3
+        moved = n * (H * D * 2 * 2 + D * 2) * 2 + n * (H * D + D) * 2 * 2   # cache rows in+out, queries in+out
+        res[name] = {"us": us, "bytes": moved, "GBps": moved / (us * 1e-6) / 1e9}
+        del kp, vp, ip
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +335,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-page-gate", action="store_true", help="skip the page-aware ranking measurement")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense full-context comparator")
+    ap.add_argument("--no-rope", action="store_true", help="skip the page2d cache-write measurement")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the chunked-prefill case (profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -528,6 +579,11 @@ def main():
         log(f"page-aware decode {pg['decode']['us']['page_aware']:.1f} us (plain {pg['decode']['us']['plain']:.1f} us); "
             f"prefill scoring+merge {pg['prefill_scoring_and_merge']['us']['page_aware']:.1f} us "
             f"(plain {pg['prefill_scoring_and_merge']['us']['plain']:.1f} us)")
+
+    if not args.no_rope:
+        result["page2d_rope_cache_write"] = run_rope(U, torch)
+        for k, v in result["page2d_rope_cache_write"].items():
+            log(f"page2d rope + cache write, {k}: {v['us']:.1f} us ({v['GBps']:.0f} GB/s)")
 
     print(json.dumps(result), flush=True)
 

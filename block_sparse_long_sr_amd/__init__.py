@@ -22,6 +22,7 @@ __all__ = [
     "workspace_size", "status_string", "last_error", "abi_version",
     "OP_INDEXER_DECODE", "OP_TOPK_DECODE", "OP_ATTN_DECODE",
     "OP_INDEXER_PREFILL", "OP_TOPK_PREFILL", "OP_ATTN_PREFILL", "OP_DENSE_ATTN_DECODE", "dense_attn_decode",
+    "rope_cache_write", "rope_queries",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +88,8 @@ _SIGS = {
     "uocr_sparse_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "uocr_topk_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "uocr_dense_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "uocr_rope_cache_write": ([_CFG, _KV, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "uocr_rope_queries": ([_CFG, ctypes.c_int32, _P, _P, _P, _P, _P], ctypes.c_int),
     "uocr_indexer_score_prefill": ([_CFG, _KV, _P, _I32, _I32, _P, _SZ, _P], ctypes.c_int),
     "uocr_block_topk_prefill": ([_CFG, _P, _SZ, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "uocr_sparse_attn_prefill": ([_CFG, _KV, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
@@ -183,6 +186,20 @@ def dense_attn_decode(cfg: SparseCfg, kv: KV, q, out, lse=None, ws=None, stream=
     ``ws`` as for the other entries: a tensor or (pointer, bytes)."""
     _check(_lib.uocr_dense_attn_decode(ctypes.byref(cfg), ctypes.byref(kv), _ptr(q), _ptr(out), _ptr(lse), _ptr(ws),
                                        _nbytes(ws), _stream(stream)), "dense_attn_decode")
+
+
+def rope_cache_write(cfg: SparseCfg, kv: KV, n: int, seq, pos, tok_pos, page_pos, k_new, v_new, kidx_new,
+                     stream=None) -> None:
+    """Rotate (page2d) and store n new tokens' K, V, indexer K into kv's pools."""
+    _check(_lib.uocr_rope_cache_write(ctypes.byref(cfg), ctypes.byref(kv), int(n), _ptr(seq), _ptr(pos), _ptr(tok_pos),
+                                      _ptr(page_pos), _ptr(k_new), _ptr(v_new), _ptr(kidx_new), _stream(stream)),
+           "rope_cache_write")
+
+
+def rope_queries(cfg: SparseCfg, n: int, tok_pos, page_pos, q=None, q_idx=None, stream=None) -> None:
+    """Rotate (page2d) n query tokens in place."""
+    _check(_lib.uocr_rope_queries(ctypes.byref(cfg), int(n), _ptr(tok_pos), _ptr(page_pos), _ptr(q), _ptr(q_idx),
+                                  _stream(stream)), "rope_queries")
 
 
 def indexer_score_prefill(cfg: SparseCfg, kv: KV, q_idx, q_start: int, T: int, cand_ws, stream=None) -> None:

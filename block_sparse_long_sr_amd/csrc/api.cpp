@@ -75,6 +75,10 @@ int check_dims(int32_t batch, int32_t max_blocks) {
   do {                                                                                 \
     if ((p) != nullptr && !aligned4(p)) return fail(UOCR_EINVAL, "%s is not 4-byte aligned", name); \
   } while (0)
+#define OPT_PTR16(p, name)                                                             \
+  do {                                                                                 \
+    if ((p) != nullptr && !aligned16(p)) return fail(UOCR_EINVAL, "%s is not 16-byte aligned", name); \
+  } while (0)
 #define TRY(expr)                  \
   do {                             \
     int _rc = (expr);              \
@@ -364,6 +368,59 @@ int uocr_sparse_attn_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, cons
   TRY(check_prefill_range(kv, q_start, T));
   if (T == 0) return ok();
   return attn_common(cfg, kv, q, block_idx, out, lse, T, 1, q_start, stream);
+}
+
+int uocr_rope_cache_write(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n, const int32_t* seq,
+                          const int32_t* pos, const int32_t* tok_pos, const int32_t* page_pos,
+                          const uint16_t* k_new, const uint16_t* v_new, const uint16_t* kidx_new, void* stream) {
+  TRY(check_cfg(cfg));
+  TRY(check_kv(kv, true, true));
+  if (n < 0) return fail(UOCR_ESHAPE, "n must be >= 0 (got %d)", n);
+  if (n == 0 || kv->batch == 0) return ok();
+  REQ_PTR4(seq, "seq");
+  REQ_PTR4(pos, "pos");
+  REQ_PTR4(tok_pos, "tok_pos");
+  REQ_PTR4(page_pos, "page_pos");
+  REQ_PTR16(k_new, "k_new");
+  REQ_PTR16(v_new, "v_new");
+  REQ_PTR16(kidx_new, "kidx_new");
+  uocr::RopeWriteArgs a{};
+  a.k_pool = const_cast<uint16_t*>(kv->k_pool);
+  a.v_pool = const_cast<uint16_t*>(kv->v_pool);
+  a.kidx_pool = const_cast<uint16_t*>(kv->kidx_pool);
+  a.block_table = kv->block_table;
+  a.seq = seq;
+  a.pos = pos;
+  a.tok_pos = tok_pos;
+  a.page_pos = page_pos;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.kidx_new = kidx_new;
+  a.num_blocks = kv->num_blocks;
+  a.batch = kv->batch;
+  a.max_blocks = kv->max_blocks;
+  a.heads = cfg->num_heads;
+  a.n = n;
+  return hip_status(uocr::launch_rope_cache_write(a, static_cast<hipStream_t>(stream)), "rope_cache_write");
+}
+
+int uocr_rope_queries(const uocr_sparse_cfg* cfg, int32_t n, const int32_t* tok_pos, const int32_t* page_pos,
+                      uint16_t* q, uint16_t* q_idx, void* stream) {
+  TRY(check_cfg(cfg));
+  if (n < 0) return fail(UOCR_ESHAPE, "n must be >= 0 (got %d)", n);
+  if (n == 0 || (q == nullptr && q_idx == nullptr)) return ok();
+  REQ_PTR4(tok_pos, "tok_pos");
+  REQ_PTR4(page_pos, "page_pos");
+  OPT_PTR16(q, "q");
+  OPT_PTR16(q_idx, "q_idx");
+  uocr::RopeQueryArgs a{};
+  a.q = q;
+  a.q_idx = q_idx;
+  a.tok_pos = tok_pos;
+  a.page_pos = page_pos;
+  a.heads = cfg->num_heads;
+  a.n = n;
+  return hip_status(uocr::launch_rope_queries(a, static_cast<hipStream_t>(stream)), "rope_queries");
 }
 
 size_t uocr_workspace_size(const uocr_sparse_cfg* cfg, int32_t op, int32_t rows, int32_t max_blocks) {

@@ -96,6 +96,36 @@ struct DenseArgs {
 };
 hipError_t launch_dense_attn(const DenseArgs& a, hipStream_t stream);
 
+// page2d rotary encoding: cache write of n new tokens and queries in place.
+struct RopeWriteArgs {
+  uint16_t* k_pool;            // [P][H][32][D], written
+  uint16_t* v_pool;            // [P][H][32][D], written
+  uint16_t* kidx_pool;         // [P][32][Di], written
+  const int32_t* block_table;  // [batch][max_blocks]
+  const int32_t* seq;          // [n]
+  const int32_t* pos;          // [n]
+  const int32_t* tok_pos;      // [n]
+  const int32_t* page_pos;     // [n]
+  const uint16_t* k_new;       // [n][H][D]
+  const uint16_t* v_new;       // [n][H][D]
+  const uint16_t* kidx_new;    // [n][Di]
+  int64_t num_blocks;
+  int32_t batch;
+  int32_t max_blocks;
+  int32_t heads;
+  int32_t n;
+};
+hipError_t launch_rope_cache_write(const RopeWriteArgs& a, hipStream_t stream);
+struct RopeQueryArgs {
+  uint16_t* q;                 // [n][H][D] or null, rotated in place
+  uint16_t* q_idx;             // [n][Di] or null, rotated in place
+  const int32_t* tok_pos;      // [n]
+  const int32_t* page_pos;     // [n]
+  int32_t heads;
+  int32_t n;
+};
+hipError_t launch_rope_queries(const RopeQueryArgs& a, hipStream_t stream);
+
 // Chunked-prefill scoring: partition of the context into splits.
 struct PrefillPlan {
   int32_t n_tiles;   // ceil(T / 256) row tiles

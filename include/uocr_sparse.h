@@ -263,6 +263,42 @@ int uocr_sparse_attn_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, cons
                              int32_t T, const int32_t* block_idx, float* out, float* lse, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------ page2d rotary + cache */
+
+/*
+ * page2d rotary position encoding (news.rkmt.cn/news/25027 Sec. 4 and
+ * Sec. 6), the step that produces the pre-rotated K the attention path reads.
+ * A 128-dim row's 64 rotation pairs (i, i+64) -- rotate-half layout, the
+ * angles cat(tok, page) doubled -- turn by tok_pos * 10000^(-2i/126) for the
+ * 63 token pairs (the token axis samples its own 126-dim spectrum) and by
+ * (page_pos mod 2) * 256^0 for the page pair.  tok_pos is the token's offset
+ * inside its page and page_pos its page number; the main attention's q/k and
+ * the indexer's q/k share them.  The rotation is computed in float64 and
+ * rounded once to bf16 (nearest, ties to even).  The coordinates are inputs:
+ * the model's token bookkeeping (page markers) that produces them is not
+ * part of this library.
+ *
+ * uocr_rope_cache_write stores n new tokens into the caches of kv: token t
+ * of sequence seq[t] at position pos[t] gets its K rows (every head) and its
+ * indexer-K row rotated and its V rows copied into pool block
+ * block_table[seq[t]][pos[t]/32], row pos[t]%32.  This entry WRITES the pools
+ * that kv points to.  Tokens whose seq, pos or pool block is out of range are
+ * skipped on the device.
+ *   seq, pos, tok_pos, page_pos : [n] int32
+ *   k_new, v_new : [n][H][D] bf16;  kidx_new : [n][Di] bf16
+ */
+int uocr_rope_cache_write(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n, const int32_t* seq,
+                          const int32_t* pos, const int32_t* tok_pos, const int32_t* page_pos,
+                          const uint16_t* k_new, const uint16_t* v_new, const uint16_t* kidx_new, void* stream);
+
+/*
+ * Rotates n query tokens in place with the same encoding:
+ *   q     : [n][H][D] bf16 or NULL;  q_idx : [n][Di] bf16 or NULL
+ *   tok_pos, page_pos : [n] int32
+ */
+int uocr_rope_queries(const uocr_sparse_cfg* cfg, int32_t n, const int32_t* tok_pos, const int32_t* page_pos,
+                      uint16_t* q, uint16_t* q_idx, void* stream);
+
 /* ------------------------------------------------------------- utilities */
 
 /*

@@ -58,11 +58,11 @@ def rope_page2d_f64(x: np.ndarray, tok_pos: int, page_pos: int) -> np.ndarray:
 
 def bf16_bits_nearest(x: np.ndarray) -> np.ndarray:
     """float64 -> bfloat16 bit patterns, rounded once to nearest (ties to
-    even).  Finite values of normal bf16 range only."""
+    even), the sign of zero kept.  Finite values of normal bf16 range only."""
     x = np.asarray(x, dtype=np.float64)
     m, e = np.frexp(x)                          # x = m * 2^e, 0.5 <= |m| < 1
     scale = np.ldexp(1.0, e - 8)                # bf16 keeps 8 significant bits
-    r = np.where(x == 0.0, 0.0, np.round(x / scale) * scale)   # np.round: half to even
+    r = np.where(x == 0.0, x, np.round(x / scale) * scale)     # np.round: half to even; zeros keep their sign
     f = r.astype(np.float32)                    # exact: r has <= 8 significant bits
     assert np.all(np.isfinite(f))
     return (f.view(np.uint32) >> 16).astype(np.uint16)

@@ -41,7 +41,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["uocr_indexer_score_decode", "uocr_block_topk_decode", "uocr_sparse_attn_decode",
-              "uocr_topk_attn_decode", "uocr_dense_attn_decode", "uocr_indexer_score_prefill", "uocr_block_topk_prefill", "uocr_sparse_attn_prefill",
+              "uocr_topk_attn_decode", "uocr_dense_attn_decode", "uocr_rope_cache_write", "uocr_rope_queries",
+              "uocr_indexer_score_prefill", "uocr_block_topk_prefill", "uocr_sparse_attn_prefill",
               "uocr_workspace_size", "uocr_status_string", "uocr_last_error", "uocr_abi_version"]:
         assert n in names
 
@@ -168,6 +169,24 @@ def test_dense_decode_argument_checks(U):
         U.dense_attn_decode(cfg, _kv(U, v_pool=None), FAKE, FAKE, ws=(FAKE, small), stream=0)
     assert e.value.status == 1 and "v_pool" in U.last_error()
     U.dense_attn_decode(cfg, _kv(U, batch=0), None, None, stream=0)   # empty batch: nothing to do
+
+
+def test_rope_argument_checks(U):
+    cfg = U.make_cfg()
+    with pytest.raises(U.UocrError) as e:
+        U.rope_cache_write(cfg, _kv(U), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, stream=0)
+    assert e.value.status == 1 and "v_new" in U.last_error()
+    with pytest.raises(U.UocrError) as e:
+        U.rope_cache_write(cfg, _kv(U, kidx_pool=None), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == 1 and "kidx_pool" in U.last_error()
+    with pytest.raises(U.UocrError) as e:
+        U.rope_cache_write(cfg, _kv(U), -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(U.UocrError) as e:
+        U.rope_queries(cfg, 3, None, FAKE, q=FAKE, stream=0)
+    assert e.value.status == 1 and "tok_pos" in U.last_error()
+    U.rope_queries(cfg, 3, None, None, stream=0)                     # nothing to rotate
+    U.rope_cache_write(cfg, _kv(U), 0, None, None, None, None, None, None, None, stream=0)
 
 
 def test_page_tags_need_query_pages(U):

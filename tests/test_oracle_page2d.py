@@ -54,7 +54,7 @@ def test_golden_rotations():
         for dim, bits in zip(pairs[0::2], pairs[1::2]):
             assert y[int(dim)] == int(bits, 16), (name, tok, page, dim, hex(y[int(dim)]))
         touched = {int(d) for d in pairs[0::2]}
-        assert all(y[d] == 0 for d in range(128) if d not in touched), name
+        assert all((y[d] & 0x7FFF) == 0 for d in range(128) if d not in touched), name   # +-0
 
 
 def test_identity_at_origin_and_even_page():
@@ -94,7 +94,7 @@ def test_bf16_rounding_is_nearest_even():
     vals = np.array([one + ulp / 2, one + 3 * ulp / 2, one + ulp / 4, -(one + ulp / 2), 0.0, -0.0,
                      one + ulp / 2 + 2.0 ** -30], np.float64)
     got = oracle.bf16_bits_nearest(vals)
-    want = [0x3F80, 0x3F82, 0x3F80, 0xBF80, 0x0000, 0x0000, 0x3F81]
+    want = [0x3F80, 0x3F82, 0x3F80, 0xBF80, 0x0000, 0x8000, 0x3F81]
     assert [int(v) for v in got] == want
     # against float32 values: exact for bf16-representable inputs
     g = np.random.default_rng(4)
