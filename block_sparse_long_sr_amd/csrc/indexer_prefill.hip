@@ -7,7 +7,7 @@
 // Work is tiled as 512 query rows x one context split per workgroup of 8
 // waves, two per SIMD; each wave holds two 32-row query tiles in registers.
 // Each 32-key block's 8 KB indexer tile is copied from memory straight into
-// one of four LDS buffers (global_load_lds, three blocks ahead, 1 KB per
+// one of eight LDS buffers (global_load_lds, six blocks ahead, 1 KB per
 // wave); each wave multiplies it with its query tiles using
 // v_mfma_f32_32x32x16_bf16 with the keys on the M axis and the queries on N.
 // A lane then holds 16 of the 32 key scores of one query column per tile,
@@ -15,10 +15,14 @@
 // lane half h owns the row of tile h.
 //
 // The two waves of a SIMD take turns: between consecutive barriers one of
-// them issues a block's products while the other runs the block max and list
-// insertion of the block it multiplied before (and reads the A fragments of
-// its next block from LDS), so the matrix unit stays busy while the vector
-// unit does the epilogue.  Blocks beyond a row's causal candidate limit
+// them issues the products of two blocks (four independent accumulator
+// chains) while the other runs the block max and list insertion of the two
+// blocks it multiplied before (and reads the A fragments of its next two
+// blocks from LDS), so the matrix unit stays busy while the vector unit does
+// the epilogue.  Both waves run the same straight-line step, the
+// second one barrier behind the first; with a single code path the compiler
+// tracks which tile buffer each LDS read depends on and leaves the copies of
+// the other buffers in flight.  Blocks beyond a row's causal candidate limit
 // (j <= (q_start+t)/32 - local) are skipped per row.  Each lane keeps a
 // sorted list of its row's best (topk - local) blocks of the split; only
 // those lists are written, never the [T, context/32] score matrix.
@@ -27,7 +31,7 @@
 // replaced by the (complemented) in-split block index.  Ranking therefore
 // uses scores truncated to 2^-(23 - idbits) relative (2^-17 at 128K
 // context), equal truncated scores going to the lower block id.  Entries are
-// unique, so a sorted insertion is one min and one max per slot.
+// unique, so a sorted insertion is one median of three per slot.
 //
 // The 128-dim contraction is split into 8 MFMA steps of 16; lane half h of an
 // operand covers dims 64h + 8s .. +8 in step s for both A and B, a consistent
@@ -46,7 +50,7 @@ constexpr int kPfWaves = kPfThreads / kWave;      // 8
 constexpr int kPfRows = kPfWaves * 64;            // 512 query rows per workgroup
 constexpr int kTileBytes = kBlock * kDim * 2;     // 8 KB indexer tile
 constexpr int kMaxBps = 1 << kMaxIdBits;          // blocks per split (pool indices in LDS)
-constexpr int kAhead = 3;                         // copies run this many blocks ahead (four buffers)
+constexpr int kAhead = 6;                         // copies run this many blocks ahead (eight buffers)
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
@@ -65,10 +69,12 @@ __device__ __forceinline__ float max16(const f32x16_t& v) {
   return fmaxf(m, v[15]);
 }
 
+// Insert kp into the descending list lk (unique entries): the new slot r is
+// the median of (old slot r-1, kp, old slot r), one v_med3_u32.
 template <int R>
 __device__ __forceinline__ void insert_sorted(uint32_t (&lk)[R], uint32_t kp) {
 #pragma unroll
-  for (int r = R - 1; r > 0; --r) lk[r] = max(lk[r], min(lk[r - 1], kp));
+  for (int r = R - 1; r > 0; --r) lk[r] = max(min(lk[r - 1], kp), min(max(lk[r - 1], kp), lk[r]));
   lk[0] = max(lk[0], kp);
 }
 
@@ -84,15 +90,17 @@ __device__ __forceinline__ int simd_turn(uint32_t* counters) {
   return (int)(__builtin_amdgcn_readfirstlane(rank) & 1u);
 }
 
-// The block loop of one workgroup.  The four tile buffers and the pool-index
-// table are separate LDS objects, so the compiler knows that reading one
-// buffer does not depend on copies still landing in another and leaves those
-// waits to the explicit counts below.
+// The block loop of one workgroup.  The eight tile buffers and the
+// pool-index table are separate LDS objects, so the compiler knows that
+// reading one buffer does not depend on copies still landing in another and
+// leaves those waits to the explicit counts below.
 template <int R>
 __device__ __forceinline__ void prefill_blocks(const IndexerPrefillArgs& a, int jb, int je, int tw, int lim,
                                                int turn, int32_t qpage, lds_u8* __restrict__ B0,
                                                lds_u8* __restrict__ B1, lds_u8* __restrict__ B2,
-                                               lds_u8* __restrict__ B3, lds_i32* __restrict__ tbl,
+                                               lds_u8* __restrict__ B3, lds_u8* __restrict__ B4,
+                                               lds_u8* __restrict__ B5, lds_u8* __restrict__ B6,
+                                               lds_u8* __restrict__ B7, lds_i32* __restrict__ tbl,
                                                lds_i32* __restrict__ tags, const unsigned char* __restrict__ pool,
                                                uint32_t (&lk)[R]) {
   const PrefillPlan& P = a.plan;
@@ -131,20 +139,22 @@ __device__ __forceinline__ void prefill_blocks(const IndexerPrefillArgs& a, int 
 #pragma unroll
   for (int s = 0; s < 8; ++s) raddr[s] = (uint32_t)(n * 256 + (((8 * h + s) ^ (n & 15)) * 16));
 
-  // Copy of block jj into buffer BUF (an invalid pool index copies pool
-  // block 0 and is flagged in okbits at bit (jj - jb) mod 64).
+  // Copy of block jj, whose pool index is PB, into buffer BUF (an invalid
+  // pool index copies pool block 0 and is flagged in okbits at bit
+  // (jj - jb) mod 64).
   const uint32_t nb32 = a.num_blocks < 0x7FFFFFFF ? (uint32_t)a.num_blocks : 0x7FFFFFFFu;
   uint64_t okbits = 0;
-#define UOCR_COPY(jj, BUF)                                                                                \
+#define UOCR_COPY(jj, BUF, PB)                                                                            \
   do {                                                                                                    \
     const int k_ = (jj) - jb;                                                                             \
-    const uint32_t pb_ = (uint32_t)__builtin_amdgcn_readfirstlane(tbl[k_]);                               \
+    const uint32_t pb_ = (PB);                                                                            \
     const bool ok_ = pb_ < nb32; /* negative indices wrap to large values */                              \
     const unsigned char* src_ = pool + (size_t)(ok_ ? pb_ : 0u) * kTileBytes;                             \
     __builtin_amdgcn_global_load_lds(src_ + goff, (BUF) + ldsoff, 16, 0, 0);                              \
     const uint64_t bit_ = 1ull << (k_ & 63);                                                              \
     okbits = (okbits & ~bit_) | (bit_ & (0ull - (uint64_t)ok_));                                          \
   } while (0)
+#define UOCR_POOL_INDEX(jj) ((uint32_t)__builtin_amdgcn_readfirstlane(tbl[(jj) - jb]))
 #define UOCR_BARRIER()                     \
   do {                                     \
     __builtin_amdgcn_sched_barrier(0);     \
@@ -153,33 +163,37 @@ __device__ __forceinline__ void prefill_blocks(const IndexerPrefillArgs& a, int 
     asm volatile("" ::: "memory");         \
     __builtin_amdgcn_sched_barrier(0);     \
   } while (0)
-#define UOCR_READ_A(BUF)                                                      \
+#define UOCR_READ_A(AV, BUF)                                                  \
   do {                                                                        \
-    _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_) av[s_] = *(lds_bf16x8*)((BUF) + raddr[s_]); \
+    _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_) AV[s_] = *(lds_bf16x8*)((BUF) + raddr[s_]); \
   } while (0)
 
-  bf16x8_t av[8];  // A fragments of the block this wave multiplies next
-  f32x16_t c0, c1;  // products of the block this wave multiplied last
+  bf16x8_t av0[8], av1[8];  // A fragments of the two blocks this wave multiplies next
+  f32x16_t c0, c1, c2, c3;  // products of the two blocks it multiplied last
 
-#define UOCR_MFMA()                                                                                       \
+#define UOCR_MFMA2()                                                                                      \
   do {                                                                                                    \
-    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[0], qf[0][0], f32x16_t{0}, 0, 0, 0);                \
-    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[0], qf[1][0], f32x16_t{0}, 0, 0, 0);                \
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av0[0], qf[0][0], f32x16_t{0}, 0, 0, 0);               \
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av0[0], qf[1][0], f32x16_t{0}, 0, 0, 0);               \
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av1[0], qf[0][0], f32x16_t{0}, 0, 0, 0);               \
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av1[0], qf[1][0], f32x16_t{0}, 0, 0, 0);               \
     _Pragma("unroll") for (int s_ = 1; s_ < 8; ++s_) {                                                    \
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s_], qf[0][s_], c0, 0, 0, 0);                      \
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[s_], qf[1][s_], c1, 0, 0, 0);                      \
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av0[s_], qf[0][s_], c0, 0, 0, 0);                     \
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av0[s_], qf[1][s_], c1, 0, 0, 0);                     \
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av1[s_], qf[0][s_], c2, 0, 0, 0);                     \
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av1[s_], qf[1][s_], c3, 0, 0, 0);                     \
     }                                                                                                     \
     /* the products belong to this half step: keep them before its barrier */                            \
-    asm volatile("" : "+v"(c0), "+v"(c1));                                                                \
+    asm volatile("" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));                                          \
   } while (0)
 
   // Block max, candidate key and sorted insertion of block JJ for this
-  // lane's row from (c0, c1).
-#define UOCR_EPI(JJ)                                                                                      \
+  // lane's row from its products (CA, CB) with query tiles 0 and 1.
+#define UOCR_EPI(JJ, CA, CB)                                                                              \
   do {                                                                                                    \
     const int jj_ = (JJ);                                                                                 \
     const bool ok_ = ((okbits >> ((jj_ - jb) & 63)) & 1ull) != 0;                                        \
-    const auto sw_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(max16(c0)), __float_as_uint(max16(c1)), \
+    const auto sw_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(max16(CA)), __float_as_uint(max16(CB)), \
                                                       false, false);                                     \
     float b_ = fmaxf(__uint_as_float(sw_[0]), __uint_as_float(sw_[1]));                                  \
     b_ = ok_ ? b_ : __builtin_nanf("");                                                                   \
@@ -198,77 +212,88 @@ __device__ __forceinline__ void prefill_blocks(const IndexerPrefillArgs& a, int 
     _Pragma("unroll") for (int r_ = 0; r_ < R; ++r_) asm volatile("" : "+v"(lk[r_]));                     \
   } while (0)
 
-  // Turn 0 multiplies block j in the first half of its step and runs its
-  // epilogue in the second; turn 1 runs block j-1's epilogue in the first
-  // half and multiplies block j in the second.  A wave starts the copy of
-  // block j+3 just before issuing block j's products and, before the barrier
-  // that ends the first half, waits for its copy of block j+1 (turn 0 has
-  // blocks j+2 and j+3 in flight after it, turn 1 only block j+2).  Buffer of
-  // block jb + k is k % 4; a buffer is refilled only after both turns have
-  // read the A fragments of its previous block.
-#define UOCR_STEP(BC, BN, BF, FIRST)                                                                      \
+  // One step for blocks j and j+1, the same for both turns: start the copies
+  // of blocks j+6 and j+7 into the buffers that held blocks j-2 and j-1
+  // (their pool indices were read from LDS in the previous step), issue the
+  // products of blocks j and j+1, barrier; read the A fragments of blocks
+  // j+2 and j+3, read the pool indices of blocks j+8 and j+9, run the
+  // epilogues of blocks j and j+1, wait for this wave's copies up to block
+  // j+5, barrier.  Turn 1 runs one barrier behind turn 0, so each wave's
+  // products overlap the other wave's epilogues.  With barriers counted from
+  // the prologue's (0) and j = jb + 2k, turn 0 multiplies between barriers 2k
+  // and 2k+1 and reads blocks j+2, j+3 after 2k+1; turn 1 multiplies between
+  // 2k+1 and 2k+2 and reads after 2k+2.  Every wave has its share of blocks
+  // up to j+3 in LDS by barrier 2k+1 (turn 0 waited at 2k, turn 1 at 2k+1),
+  // and all reads of blocks j-2 and j-1 complete before barrier 2k-1, before
+  // their buffers are refilled after barrier 2k.  Buffer of block jb + i is
+  // i % 8.
+#define UOCR_STEP(BN0, BN1, BF0, BF1)                                                                     \
   do {                                                                                                    \
-    if (turn == 0) {                                                                                      \
-      UOCR_COPY(min(j + kAhead, je - 1), BF);                                                             \
-      UOCR_MFMA();                                                                                        \
-      UOCR_WAIT_VM(kAhead - 1);                                                                           \
-      UOCR_BARRIER();                                                                                     \
-      UOCR_READ_A(BN);                                                                                    \
-      UOCR_EPI(j);                                                                                        \
-      UOCR_WAIT_LGKM0();                                                                                  \
-      UOCR_BARRIER();                                                                                     \
-    } else {                                                                                              \
-      UOCR_READ_A(BC);                                                                                    \
-      if (!(FIRST)) UOCR_EPI(j - 1);                                                                      \
-      UOCR_WAIT_VM(kAhead - 2);                                                                           \
-      UOCR_WAIT_LGKM0();                                                                                  \
-      UOCR_BARRIER();                                                                                     \
-      UOCR_COPY(min(j + kAhead, je - 1), BF);                                                             \
-      UOCR_MFMA();                                                                                        \
-      UOCR_BARRIER();                                                                                     \
-    }                                                                                                     \
-    ++j;                                                                                                  \
+    UOCR_COPY(min(j + kAhead, je - 1), BF0, pb0);                                                         \
+    UOCR_COPY(min(j + kAhead + 1, je - 1), BF1, pb1);                                                     \
+    UOCR_MFMA2();                                                                                         \
+    UOCR_WAIT_VM(kAhead - 2);                                                                             \
+    UOCR_BARRIER();                                                                                       \
+    UOCR_READ_A(av0, BN0);                                                                                \
+    UOCR_READ_A(av1, BN1);                                                                                \
+    const int32_t t0_ = tbl[min(j + kAhead + 2, je - 1) - jb];                                            \
+    const int32_t t1_ = tbl[min(j + kAhead + 3, je - 1) - jb];                                            \
+    UOCR_EPI(j, c0, c1);                                                                                  \
+    UOCR_EPI(j + 1, c2, c3);                                                                              \
+    UOCR_WAIT_VM(kAhead - 4);                                                                             \
+    UOCR_WAIT_LGKM0();                                                                                    \
+    pb0 = (uint32_t)__builtin_amdgcn_readfirstlane(t0_);                                                  \
+    pb1 = (uint32_t)__builtin_amdgcn_readfirstlane(t1_);                                                  \
+    UOCR_BARRIER();                                                                                       \
+    j += 2;                                                                                               \
   } while (0)
 
-  // Prologue: blocks jb .. jb+2 (copies past the split re-read its last
-  // block and are never used); turn 0 also reads block jb's A fragments.
-  UOCR_COPY(jb, B0);
-  UOCR_COPY(min(jb + 1, je - 1), B1);
-  UOCR_COPY(min(jb + 2, je - 1), B2);
-  UOCR_WAIT_VM(kAhead - 1);
+  // Prologue: copies of blocks jb .. jb+5 (copies past the split re-read its
+  // last block and are never used); blocks jb .. jb+3 land before the first
+  // barrier, after which both turns read the A fragments of blocks jb, jb+1.
+  uint32_t pb0 = UOCR_POOL_INDEX(min(jb + kAhead, je - 1));
+  uint32_t pb1 = UOCR_POOL_INDEX(min(jb + kAhead + 1, je - 1));
+  UOCR_COPY(jb, B0, UOCR_POOL_INDEX(jb));
+  UOCR_COPY(min(jb + 1, je - 1), B1, UOCR_POOL_INDEX(min(jb + 1, je - 1)));
+  UOCR_COPY(min(jb + 2, je - 1), B2, UOCR_POOL_INDEX(min(jb + 2, je - 1)));
+  UOCR_COPY(min(jb + 3, je - 1), B3, UOCR_POOL_INDEX(min(jb + 3, je - 1)));
+  UOCR_COPY(min(jb + 4, je - 1), B4, UOCR_POOL_INDEX(min(jb + 4, je - 1)));
+  UOCR_COPY(min(jb + 5, je - 1), B5, UOCR_POOL_INDEX(min(jb + 5, je - 1)));
+  UOCR_WAIT_VM(kAhead - 4);
   UOCR_BARRIER();
-  if (turn == 0) UOCR_READ_A(B0);
+  UOCR_READ_A(av0, B0);
+  UOCR_READ_A(av1, B1);
+  UOCR_WAIT_LGKM0();
+  if (turn != 0) UOCR_BARRIER();
 
   int j = jb;
-  // Whole groups of four steps; steps past the split's last block compute on
-  // re-read tiles whose keys the row limit (capped at je - 1) discards.
-  UOCR_STEP(B0, B1, B3, true);
-  UOCR_STEP(B1, B2, B0, false);
-  UOCR_STEP(B2, B3, B1, false);
-  UOCR_STEP(B3, B0, B2, false);
-  while (j < je) {
-    UOCR_STEP(B0, B1, B3, false);
-    UOCR_STEP(B1, B2, B0, false);
-    UOCR_STEP(B2, B3, B1, false);
-    UOCR_STEP(B3, B0, B2, false);
-  }
-  if (turn != 0) UOCR_EPI(j - 1);
+  // Whole groups of eight blocks; steps past the split's last block compute
+  // on re-read tiles whose keys the row limit (capped at je - 1) discards.
+  do {
+    UOCR_STEP(B2, B3, B6, B7);
+    UOCR_STEP(B4, B5, B0, B1);
+    UOCR_STEP(B6, B7, B2, B3);
+    UOCR_STEP(B0, B1, B4, B5);
+  } while (j < je);
+  // Both turns pass the same number of barriers.
+  if (turn == 0) UOCR_BARRIER();
   // No copy may still be landing in LDS when the workgroup ends.
   UOCR_WAIT_VM(0);
 #undef UOCR_STEP
 #undef UOCR_EPI
-#undef UOCR_MFMA
+#undef UOCR_MFMA2
 #undef UOCR_READ_A
 #undef UOCR_BARRIER
+#undef UOCR_POOL_INDEX
 #undef UOCR_COPY
 }
 
 template <int R>
 __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerPrefillArgs a) {
-  // Four tile buffers as separate objects: the compiler then knows that an
+  // Eight tile buffers as separate objects: the compiler then knows that an
   // LDS read of one buffer never depends on a copy landing in another.
   __shared__ __attribute__((aligned(16))) unsigned char tb0[kTileBytes], tb1[kTileBytes], tb2[kTileBytes],
-      tb3[kTileBytes];
+      tb3[kTileBytes], tb4[kTileBytes], tb5[kTileBytes], tb6[kTileBytes], tb7[kTileBytes];
   __shared__ int32_t s_tbl[kMaxBps];  // pool indices of the split's blocks
   __shared__ int32_t s_tag[kMaxBps];  // page tags of the split's blocks (page-aware ranking)
   __shared__ uint32_t s_turns[4];
@@ -307,10 +332,12 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
   if (jb < je) {
     const int32_t qpage = (a.block_page != nullptr && row < a.T) ? a.row_page[row] : 0;
     prefill_blocks<R>(a, jb, je, tw, lim, turn, qpage, (lds_u8*)tb0, (lds_u8*)tb1, (lds_u8*)tb2, (lds_u8*)tb3,
-                      (lds_i32*)s_tbl, (lds_i32*)s_tag, reinterpret_cast<const unsigned char*>(a.kidx_pool), lk);
+                      (lds_u8*)tb4, (lds_u8*)tb5, (lds_u8*)tb6, (lds_u8*)tb7, (lds_i32*)s_tbl, (lds_i32*)s_tag, reinterpret_cast<const unsigned char*>(a.kidx_pool), lk);
   }
+  // Lists are stored split-major, [nsplit][T][R]: the 64 consecutive rows of
+  // a wave write one contiguous run.
   if (row < a.T) {
-    uint32_t* dst = a.cand_keys + ((size_t)row * P.nsplit + split) * R;
+    uint32_t* dst = a.cand_keys + ((size_t)split * a.T + row) * R;
 #pragma unroll
     for (int r = 0; r < R; ++r) dst[r] = lk[r];
   }
@@ -387,7 +414,7 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(TopkPrefillArgs a) {
   const uint32_t idmask = (1u << P.idbits) - 1u;
   uint32_t lk[R];
   int32_t li[R];
-  const size_t off = ((size_t)t * P.nsplit + lane) * R;
+  const size_t off = ((size_t)lane * a.T + t) * R;  // [nsplit][T][R]
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t kp = lane < P.nsplit ? a.cand_keys[off + r] : 0u;

@@ -141,7 +141,7 @@ struct IndexerPrefillArgs {
   const uint16_t* kidx_pool;
   const int32_t* block_table;  // row of sequence 0
   const uint16_t* q_idx;       // [T][128]
-  uint32_t* cand_keys;         // [T][nsplit][R] packed keys, 0 = empty
+  uint32_t* cand_keys;         // [nsplit][T][R] packed keys, 0 = empty
   int64_t num_blocks;
   int32_t T;
   int32_t q_start;
