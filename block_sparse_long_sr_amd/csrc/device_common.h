@@ -51,6 +51,12 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 __device__ __forceinline__ float shfl_xor_f32(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// Block-max reduction of key scores: NaN-propagating maximum (a block with a
+// NaN key scores NaN, like a maximum over the set taken in the plain
+// definition; ranked last).  On gfx950 it is v_maximum(3)_f32, with no
+// operand canonicalisation.
+__device__ __forceinline__ float max_keep_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Order-preserving map float32 -> uint32: a > b (as numbers) <=> key(a) >
 // key(b); -0.0 maps like +0.0; NaN maps to 0, below every number.
 __device__ __forceinline__ uint32_t order_key(float f) {

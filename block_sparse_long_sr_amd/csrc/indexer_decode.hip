@@ -49,9 +49,9 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerDecodeArgs a
       for (int k = 0; k < 8; ++k) kv[k] = base[k * kWave + lane];
       float m = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) m = fmaxf(m, row16_sum(dot8_bf16(kv[k], qv)));
-      m = fmaxf(m, shfl_xor_f32(m, 16));
-      m = fmaxf(m, shfl_xor_f32(m, 32));
+      for (int k = 0; k < 8; ++k) m = max_keep_nan(m, row16_sum(dot8_bf16(kv[k], qv)));
+      m = max_keep_nan(m, shfl_xor_f32(m, 16));
+      m = max_keep_nan(m, shfl_xor_f32(m, 32));
       score = m;
     }
     if (lane == 0) out[j] = score;

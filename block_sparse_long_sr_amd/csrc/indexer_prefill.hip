@@ -63,10 +63,10 @@ typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
 #define UOCR_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
 
 __device__ __forceinline__ float max16(const f32x16_t& v) {
-  float m = fmaxf(fmaxf(v[0], v[1]), v[2]);
+  float m = max_keep_nan(max_keep_nan(v[0], v[1]), v[2]);
 #pragma unroll
-  for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, v[r]), v[r + 1]);
-  return fmaxf(m, v[15]);
+  for (int r = 3; r < 15; r += 2) m = max_keep_nan(max_keep_nan(m, v[r]), v[r + 1]);
+  return max_keep_nan(m, v[15]);
 }
 
 // Insert kp into the descending list lk (unique entries): the new slot r is
@@ -195,7 +195,7 @@ __device__ __forceinline__ void prefill_blocks(const IndexerPrefillArgs& a, int 
     const bool ok_ = ((okbits >> ((jj_ - jb) & 63)) & 1ull) != 0;                                        \
     const auto sw_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(max16(CA)), __float_as_uint(max16(CB)), \
                                                       false, false);                                     \
-    float b_ = fmaxf(__uint_as_float(sw_[0]), __uint_as_float(sw_[1]));                                  \
+    float b_ = max_keep_nan(__uint_as_float(sw_[0]), __uint_as_float(sw_[1]));                           \
     b_ = ok_ ? b_ : __builtin_nanf("");                                                                   \
     const uint32_t idmask_ = (1u << P.idbits) - 1u;                                                      \
     uint32_t o_ = order_key(b_);                                                                          \

@@ -139,7 +139,8 @@ typedef struct uocr_kv {
  *   block_scores : [batch][max_blocks] float32, written.  For sequence b with
  *                  p = ctx_len-1 and nb = p/32+1 blocks, entry j < nb-local
  *                  (a remote candidate) is max over the block's 32 keys of
- *                  q_idx . kidx (float32 accumulation of exact bf16 products);
+ *                  q_idx . kidx (float32 accumulation of exact bf16 products;
+ *                  NaN if any of the 32 scores is NaN, which ranks last);
  *                  every other entry is -inf.
  * Uses the k_pool/v_pool fields of kv only for validation (may be NULL).
  */

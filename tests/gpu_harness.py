@@ -140,6 +140,8 @@ def check_scores(gpu_scores_row: np.ndarray, ref: Dict, q_idx_bits, kidx_bits, m
     o = ref["block_scores"].astype(np.float64)
     g = gpu_scores_row[:ncand].astype(np.float64)
     tol = score_bound(q_idx_bits, kidx_bits, ncand) + np.abs(o) * 2.0**-23
+    assert np.array_equal(np.isnan(g), np.isnan(o)), \
+        f"NaN block scores differ: gpu {np.nonzero(np.isnan(g))[0][:8]} oracle {np.nonzero(np.isnan(o))[0][:8]}"
     bad = np.abs(g - o) > tol
     assert not bad.any(), f"{bad.sum()} block scores out of bound, first at {np.argmax(bad)}: gpu {g[bad][0]} oracle {o[bad][0]}"
     assert np.all(np.isneginf(gpu_scores_row[ncand:max_blocks])), "non-candidate entries must be -inf"

@@ -230,3 +230,33 @@ def test_fused_select_attention_rejects_unsupported():
                            torch.zeros(1, 300, dtype=torch.int32, device="cuda"),
                            torch.zeros(1, 10, 128, device="cuda"))
     assert e.value.status == 5
+
+
+def test_nan_key_in_candidate_block_ranks_last():
+    """A NaN indexer key inside a remote candidate block: the block max over
+    its 32 scores is NaN, and a NaN score ranks last (news.rkmt.cn/news/25027
+    Sec. 5 step 2, the block score as the maximum of its keys' scores; the
+    ranking rule for NaN is this path's documented reading).  Oracle and
+    kernel must agree on which blocks are NaN and on the selection."""
+    wl = _wl("nan key", 0xE7, [4000, 3000])
+    print("case: decode NaN indexer key in candidate blocks", flush=True)
+    dev = SD.generate(wl)
+    cfg_u, cfg_o = G.cfg_for(wl), G.ocfg()
+    tab = dev.block_table.cpu().numpy()
+    planted = {0: [(5, 3), (40, 31)], 1: [(0, 0), (70, 17)]}  # (block, key in block)
+    kidx_host = {}
+    for b, lst in planted.items():
+        kid = wl.kidx(0, b, 0, int(wl.ctx_lens[b])).copy()
+        for j, i in lst:
+            kid[32 * j + i, 7] = 0x7FC0  # one NaN dimension
+            dev.kidx[0][int(tab[b, j]), i, 7] = 0x7FC0
+        kidx_host[b] = kid
+    torch.cuda.synchronize()
+    res = G.gpu_decode(dev, 0, cfg_u)
+    for b, lst in planted.items():
+        ref = G.oracle_decode(wl, 0, b, cfg_o, kidx=kidx_host[b])
+        G.check_scores(res["scores"][b], ref, wl.q_idx(0, b), kidx_host[b], wl.max_blocks)
+        G.check_selection(res["idx"][b], ref, cfg_u.topk_blocks)
+        for j, _ in lst:
+            assert np.isnan(ref["block_scores"][j]) and np.isnan(res["scores"][b, j])
+            assert j not in ref["selected"] and j not in res["idx"][b]

@@ -79,3 +79,31 @@ def test_prefill_64_splits_sampled():
     print("case:", wl.name, flush=True)
     rows = sorted(set([0, 1, 31, 32, 255, 256, 511, 1023, 1024, 2047] + list(range(5, 2048, 97))))
     check_prefill(wl, rows)
+
+
+def test_prefill_nan_key_in_candidate_block_ranks_last():
+    """As the decode case: a NaN indexer key makes its block's score NaN in
+    the MFMA scoring too, and that block ranks last for every row."""
+    wl = W.prefill_case("prefill NaN key", 0xF7, 3000, 2200, 300)
+    print("case:", wl.name, flush=True)
+    cfg_u, cfg_o = G.cfg_for(wl), G.ocfg()
+    dev = SD.generate(wl)
+    tab = dev.block_table.cpu().numpy()
+    S = int(wl.ctx_lens[0])
+    kid = wl.kidx(0, 0, 0, S).copy()
+    nan_blocks = [3, 50]
+    for j, i in zip(nan_blocks, [9, 0]):
+        kid[32 * j + i, 100] = 0x7FC0
+        dev.kidx[0][int(tab[0, j]), i, 100] = 0x7FC0
+    torch.cuda.synchronize()
+    res = G.gpu_prefill(dev, cfg_u)
+    rows = list(range(0, wl.rows, 7)) + [wl.rows - 1]
+    allrows = np.arange(wl.rows)
+    refs = oracle.prefill_rows_fetch(wl.q_rows(allrows), wl.q_idx_rows(allrows), kid, G.fetcher(wl, 0, 0),
+                                     wl.q_start, rows, cfg_o)
+    for r in refs:
+        t = r["row"]
+        G.check_selection(res["idx"][t], r, cfg_u.topk_blocks)
+        for j in nan_blocks:
+            assert np.isnan(r["block_scores"][j])
+            assert j not in r["selected"] and j not in res["idx"][t]
