@@ -160,15 +160,22 @@ def run_prefill(U, SD, W, torch, iters=5):
     t_sc = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(2, iters + 2)) / iters
     t_mg = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(2, iters + 2)) / iters
     t_at = sum(ev[i][2].elapsed_time(ev[i][3]) for i in range(2, iters + 2)) / iters
-    # Scoring kernel alone: one event pair around back-to-back launches.
-    nrep = 10
-    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a_.record(stream)
-    for _ in range(nrep):
+    # Scoring kernel alone, in steady state: 400 untimed launches (about 20
+    # ms: under sustained matrix load the clock first drops, then settles
+    # over about 10 ms), then seven batches of 10 back-to-back launches, one
+    # event pair per batch; the median batch is reported, all seven are kept.
+    nrep, nbatch = 10, 7
+    for _ in range(400):
         U.indexer_score_prefill(cfg, kv, dev.q_idx, wl.q_start, T, wsarg, stream=sh)
-    b_.record(stream)
+    bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nbatch)]
+    for a_, b_ in bev:
+        a_.record(stream)
+        for _ in range(nrep):
+            U.indexer_score_prefill(cfg, kv, dev.q_idx, wl.q_start, T, wsarg, stream=sh)
+        b_.record(stream)
     torch.cuda.synchronize()
-    t_sc_alone = a_.elapsed_time(b_) / nrep
+    batches = [a_.elapsed_time(b_) / nrep for a_, b_ in bev]
+    t_sc_alone = sorted(batches)[nbatch // 2]
     # algorithmic work of the scoring kernel: every candidate (row, block) pair
     rowblocks = sum(max(0, (wl.q_start + t) // 32 + 1 - 4) for t in range(T))
     flops = rowblocks * 32 * 128 * 2
@@ -179,6 +186,7 @@ def run_prefill(U, SD, W, torch, iters=5):
         "rows": T,
         "tokens_per_s": T / ((t_sc + t_mg + t_at) * 1e-3),
         "ms": {"scoring": t_sc, "merge": t_mg, "attention": t_at, "scoring_back_to_back": t_sc_alone},
+        "scoring_back_to_back_batches_ms": batches,
         "scoring_in_step_TFLOPs": flops / (t_sc * 1e-3) / 1e12,
         "scoring_roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS,

@@ -93,8 +93,9 @@ __device__ __forceinline__ int simd_turn(uint32_t* counters) {
 // The block loop of one workgroup.  The eight tile buffers and the
 // pool-index table are separate LDS objects, so the compiler knows that
 // reading one buffer does not depend on copies still landing in another and
-// leaves those waits to the explicit counts below.
-template <int R>
+// leaves those waits to the explicit counts below.  GATE selects the
+// page-aware ranking at compile time, keeping its test out of the loop.
+template <int R, bool GATE>
 __device__ __forceinline__ void prefill_blocks(const IndexerPrefillArgs& a, int jb, int je, int tw, int lim,
                                                int turn, int32_t qpage, lds_u8* __restrict__ B0,
                                                lds_u8* __restrict__ B1, lds_u8* __restrict__ B2,
@@ -111,10 +112,9 @@ __device__ __forceinline__ void prefill_blocks(const IndexerPrefillArgs& a, int 
   const int h = lane >> 5;
   const int n = lane & 31;
 
-  const bool gate = a.block_page != nullptr;  // page-aware ranking
   for (int i = tid; i < je - jb; i += kPfThreads) {
     tbl[i] = a.block_table[jb + i];
-    if (gate) tags[i] = a.block_page[jb + i];
+    if (GATE) tags[i] = a.block_page[jb + i];
   }
 
   // Resident query fragments: tile c, step s -> dims 64h + 8s .. +8 of row
@@ -199,13 +199,13 @@ __device__ __forceinline__ void prefill_blocks(const IndexerPrefillArgs& a, int 
     b_ = ok_ ? b_ : __builtin_nanf("");                                                                   \
     const uint32_t idmask_ = (1u << P.idbits) - 1u;                                                      \
     uint32_t o_ = order_key(b_);                                                                          \
-    if (gate) { /* page tier in the top bit, the score's order key below it */                           \
+    if (GATE) { /* page tier in the top bit, the score's order key below it */                           \
       const bool tier_ = tags[jj_ - jb] == qpage;                                                         \
       o_ = tier_ ? (0x80000000u | (o_ >> 1)) : (o_ >> 1);                                                 \
     }                                                                                                     \
-    const uint32_t k_ = o_ > 1u ? o_ : 1u; /* empty slots are 0 */                                        \
-    /* NaN (key 1) stays above empty: the order bits are at least idmask + 1 */                          \
-    uint32_t p_ = ((k_ > idmask_ ? k_ : idmask_ + 1u) & ~idmask_) | (idmask_ - (uint32_t)(jj_ - jb));    \
+    /* empty slots are 0; the order bits are raised to at least idmask + 1 so */                         \
+    /* that every candidate, NaN (order key 0) included, stays above empty */                             \
+    uint32_t p_ = (max(o_, idmask_ + 1u) & ~idmask_) | (idmask_ - (uint32_t)(jj_ - jb));                 \
     p_ = jj_ <= lim ? p_ : 0u; /* rows past T have lim = -1 */                                            \
     insert_sorted<R>(lk, p_);                                                                             \
     /* the insertion belongs to this half step as well */                                                 \
@@ -288,7 +288,7 @@ __device__ __forceinline__ void prefill_blocks(const IndexerPrefillArgs& a, int 
 #undef UOCR_COPY
 }
 
-template <int R>
+template <int R, bool GATE>
 __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerPrefillArgs a) {
   // Eight tile buffers as separate objects: the compiler then knows that an
   // LDS read of one buffer never depends on a copy landing in another.
@@ -330,8 +330,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerP
 #pragma unroll
   for (int r = 0; r < R; ++r) lk[r] = 0u;
   if (jb < je) {
-    const int32_t qpage = (a.block_page != nullptr && row < a.T) ? a.row_page[row] : 0;
-    prefill_blocks<R>(a, jb, je, tw, lim, turn, qpage, (lds_u8*)tb0, (lds_u8*)tb1, (lds_u8*)tb2, (lds_u8*)tb3,
+    const int32_t qpage = (GATE && row < a.T) ? a.row_page[row] : 0;
+    prefill_blocks<R, GATE>(a, jb, je, tw, lim, turn, qpage, (lds_u8*)tb0, (lds_u8*)tb1, (lds_u8*)tb2, (lds_u8*)tb3,
                       (lds_u8*)tb4, (lds_u8*)tb5, (lds_u8*)tb6, (lds_u8*)tb7, (lds_i32*)s_tbl, (lds_i32*)s_tag, reinterpret_cast<const unsigned char*>(a.kidx_pool), lk);
   }
   // Lists are stored split-major, [nsplit][T][R]: the 64 consecutive rows of
@@ -375,8 +375,13 @@ hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t strea
   const int nsplit_pad = (P.nsplit + 7) / 8 * 8;
   dim3 grid(P.n_tiles * nsplit_pad);
   switch (P.R) {
-#define UOCR_CASE(RR) \
-  case RR: hipLaunchKernelGGL(indexer_prefill_kernel<RR>, grid, dim3(kPfThreads), 0, stream, a); break;
+#define UOCR_CASE(RR)                                                                                   \
+  case RR:                                                                                              \
+    if (a.block_page != nullptr)                                                                        \
+      hipLaunchKernelGGL((indexer_prefill_kernel<RR, true>), grid, dim3(kPfThreads), 0, stream, a);     \
+    else                                                                                                \
+      hipLaunchKernelGGL((indexer_prefill_kernel<RR, false>), grid, dim3(kPfThreads), 0, stream, a);    \
+    break;
     UOCR_CASE(1) UOCR_CASE(2) UOCR_CASE(3) UOCR_CASE(4) UOCR_CASE(5) UOCR_CASE(6) UOCR_CASE(7) UOCR_CASE(8)
     UOCR_CASE(9) UOCR_CASE(10) UOCR_CASE(11) UOCR_CASE(12) UOCR_CASE(13) UOCR_CASE(14) UOCR_CASE(15)
     UOCR_CASE(16)
