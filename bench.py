@@ -34,6 +34,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 KERNEL_SOURCES = {
     "indexer_decode": ["block_sparse_long_sr_amd/csrc/indexer_decode.hip",
                        "block_sparse_long_sr_amd/csrc/device_common.h"],
+    "indexer_prefill": ["block_sparse_long_sr_amd/csrc/indexer_prefill.hip",
+                        "block_sparse_long_sr_amd/csrc/device_common.h"],
 }
 
 
@@ -67,7 +69,8 @@ def decode_bytes(wl, cfg_topk=16, local=4, heads=10, D=128, Di=128):
     return idx_b, topk_b, attn_b
 
 
-TRAFFIC_FILES = {"indexer_decode": "profiles/indexer_score_decode_128k_traffic.txt"}
+TRAFFIC_FILES = {"indexer_decode": "profiles/indexer_score_decode_128k_traffic.txt",
+                 "indexer_prefill": "profiles/indexer_score_prefill_2048_traffic.txt"}
 
 
 def traffic_for(kernel):
@@ -190,7 +193,7 @@ def run_prefill(U, SD, W, torch, iters=5):
         "scoring_in_step_TFLOPs": flops / (t_sc * 1e-3) / 1e12,
         "scoring_roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS,
-                             "flops_per_launch": flops, "traffic": None},
+                             "flops_per_launch": flops, "traffic": traffic_for("indexer_prefill")},
         "attention_gathered_GBps": T * 2 * 512 * 10 * 128 * 2 / (t_at * 1e-3) / 1e9,
         "attention_unique_bytes_upper": attn_unique,
     }
