@@ -147,6 +147,8 @@ def run_prefill(U, SD, W, torch, iters=5):
     idx = torch.empty((T, 16), dtype=torch.int32, device="cuda")
     out = torch.empty((T, 10, 128), dtype=torch.float32, device="cuda")
     lse = torch.empty((T, 10), dtype=torch.float32, device="cuda")
+    # block-major attention: (row, slot) pairs bucketed by block, per-slot partials, merge
+    aws = torch.empty(U.workspace_size(cfg, U.OP_ATTN_PREFILL, T, M), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters + 2)]
@@ -157,7 +159,7 @@ def run_prefill(U, SD, W, torch, iters=5):
         e[1].record(stream)
         U.block_topk_prefill(cfg, wsarg, wl.q_start, T, M, idx, stream=sh)
         e[2].record(stream)
-        U.sparse_attn_prefill(cfg, kv, dev.q, wl.q_start, T, idx, out, lse, stream=sh)
+        U.sparse_attn_prefill(cfg, kv, dev.q, wl.q_start, T, idx, out, lse, ws=aws, stream=sh)
         e[3].record(stream)
     torch.cuda.synchronize()
     t_sc = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(2, iters + 2)) / iters
@@ -197,7 +199,7 @@ def run_prefill(U, SD, W, torch, iters=5):
         "attention_gathered_GBps": T * 2 * 512 * 10 * 128 * 2 / (t_at * 1e-3) / 1e9,
         "attention_unique_bytes_upper": attn_unique,
     }
-    del dev, ws, out
+    del dev, ws, aws, out
     torch.cuda.empty_cache()
     return res
 

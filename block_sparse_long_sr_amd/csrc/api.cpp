@@ -179,7 +179,8 @@ int uocr_block_topk_decode(const uocr_sparse_cfg* cfg, const float* block_scores
 }
 
 static int attn_common(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q, const int32_t* block_idx,
-                       float* out, float* lse, int32_t nq, int prefill, int32_t q_start, void* stream) {
+                       float* out, float* lse, int32_t nq, int prefill, int32_t q_start, void* ws, size_t ws_bytes,
+                       void* stream) {
   REQ_PTR16(q, "q");
   REQ_PTR4(block_idx, "block_idx");
   REQ_PTR4(out, "out");
@@ -201,6 +202,20 @@ static int attn_common(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint
   a.scale_log2 = cfg->sm_scale * 1.44269504088896340736f;
   a.prefill = prefill;
   a.q_start = q_start;
+  if (prefill && ws != nullptr) {
+    const uocr::PrefillAttnPlan P = uocr::prefill_attn_plan(nq, cfg->num_heads, cfg->topk_blocks, kv->max_blocks);
+    if (P.ws_bytes > 0) {
+      if (ws_bytes < P.ws_bytes)
+        return fail(UOCR_EWORKSPACE, "ws holds %zu bytes, block-major prefill attention needs %zu", ws_bytes,
+                    P.ws_bytes);
+      if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(UOCR_EINVAL, "ws must be 256-byte aligned");
+      uocr::PrefillAttnArgs pa{};
+      pa.attn = a;
+      pa.ws = ws;
+      pa.plan = P;
+      return hip_status(uocr::launch_attn_prefill_blocks(pa, static_cast<hipStream_t>(stream)), "sparse_attn_prefill");
+    }
+  }
   return hip_status(uocr::launch_attn(a, static_cast<hipStream_t>(stream)),
                     prefill ? "sparse_attn_prefill" : "sparse_attn_decode");
 }
@@ -214,7 +229,7 @@ int uocr_sparse_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const
   TRY(check_kv(kv, false, true));
   if (kv->batch == 0) return ok();
   REQ_PTR4(kv->ctx_lens, "kv->ctx_lens");
-  return attn_common(cfg, kv, q, block_idx, out, lse, kv->batch, 0, 0, stream);
+  return attn_common(cfg, kv, q, block_idx, out, lse, kv->batch, 0, 0, nullptr, 0, stream);
 }
 
 int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q,
@@ -361,13 +376,11 @@ int uocr_block_topk_prefill(const uocr_sparse_cfg* cfg, const void* cand_ws, siz
 int uocr_sparse_attn_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q, int32_t q_start,
                              int32_t T, const int32_t* block_idx, float* out, float* lse, void* ws, size_t ws_bytes,
                              void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   TRY(check_cfg(cfg));
   TRY(check_kv(kv, false, true));
   TRY(check_prefill_range(kv, q_start, T));
   if (T == 0) return ok();
-  return attn_common(cfg, kv, q, block_idx, out, lse, T, 1, q_start, stream);
+  return attn_common(cfg, kv, q, block_idx, out, lse, T, 1, q_start, ws, ws_bytes, stream);
 }
 
 int uocr_rope_cache_write(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n, const int32_t* seq,
@@ -428,6 +441,8 @@ size_t uocr_workspace_size(const uocr_sparse_cfg* cfg, int32_t op, int32_t rows,
   switch (op) {
     case UOCR_OP_DENSE_ATTN_DECODE:
       return uocr::dense_plan(rows, cfg->num_heads, max_blocks).ws_bytes;
+    case UOCR_OP_ATTN_PREFILL:
+      return uocr::prefill_attn_plan(rows, cfg->num_heads, cfg->topk_blocks, max_blocks).ws_bytes;
     case UOCR_OP_INDEXER_PREFILL:
     case UOCR_OP_TOPK_PREFILL:
       if (cfg->topk_blocks - cfg->local_blocks > kMaxRemotePrefill || max_blocks > kMaxBlocksPrefill) return 0;

@@ -16,18 +16,25 @@
 
 namespace uocr {
 
-__device__ __forceinline__ void attend_block(const uint16_t* k_tile, const uint16_t* v_tile, int j, int p,
-                                             const uint4& qv, float scale_log2, float& m, float& l, float (&o)[8]) {
+// The wave's share of a block's K and V tiles: lane l holds dims
+// 8*(l%16)..+8 of keys 4k + l/16, k = 0..7 (eight 1 KB loads per tile).
+__device__ __forceinline__ void load_block_tiles(const uint16_t* k_tile, const uint16_t* v_tile, uint4 (&kv)[8],
+                                                 uint4 (&vv)[8]) {
   const int lane = lane_id();
-  const int g = lane >> 4;  // key row group within a 4-key slab
   const uint4* kt = reinterpret_cast<const uint4*>(k_tile);
   const uint4* vt = reinterpret_cast<const uint4*>(v_tile);
-  uint4 kv[8], vv[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) kv[k] = kt[k * kWave + lane];
 #pragma unroll
   for (int k = 0; k < 8; ++k) vv[k] = vt[k * kWave + lane];
+}
 
+// Online-softmax update of (m, l, o) with block j of a query at position p,
+// from tiles already in registers.
+__device__ __forceinline__ void attend_loaded_block(const uint4 (&kv)[8], const uint4 (&vv)[8], int j, int p,
+                                                    const uint4& qv, float scale_log2, float& m, float& l,
+                                                    float (&o)[8]) {
+  const int g = lane_id() >> 4;  // key row group within a 4-key slab
   const bool full = j * kBlock + (kBlock - 1) <= p;
   float s[8];
   float bm = -INFINITY;
@@ -38,8 +45,8 @@ __device__ __forceinline__ void attend_block(const uint16_t* k_tile, const uint1
     s[k] = z;
     bm = fmaxf(bm, z);
   }
-  bm = fmaxf(bm, shfl_xor_f32(bm, 16));
-  bm = fmaxf(bm, shfl_xor_f32(bm, 32));
+  bm = max_xor16(bm);
+  bm = max_xor32(bm);
   const float m_new = fmaxf(m, bm);
   const float alpha = exp2f(m - m_new);
   l *= alpha;
@@ -64,14 +71,21 @@ __device__ __forceinline__ void attend_block(const uint16_t* k_tile, const uint1
   m = m_new;
 }
 
+__device__ __forceinline__ void attend_block(const uint16_t* k_tile, const uint16_t* v_tile, int j, int p,
+                                             const uint4& qv, float scale_log2, float& m, float& l, float (&o)[8]) {
+  uint4 kv[8], vv[8];
+  load_block_tiles(k_tile, v_tile, kv, vv);
+  attend_loaded_block(kv, vv, j, p, qv, scale_log2, m, l, o);
+}
+
 // Sum of a wave's four key groups (lanes l, l^16, l^32, l^48) of l and o.
 __device__ __forceinline__ void reduce_key_groups(float& l, float (&o)[8]) {
-  l += shfl_xor_f32(l, 16);
-  l += shfl_xor_f32(l, 32);
+  l = sum_xor16(l);
+  l = sum_xor32(l);
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
-    o[d] += shfl_xor_f32(o[d], 16);
-    o[d] += shfl_xor_f32(o[d], 32);
+    o[d] = sum_xor16(o[d]);
+    o[d] = sum_xor32(o[d]);
   }
 }
 

@@ -51,6 +51,34 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 __device__ __forceinline__ float shfl_xor_f32(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// Combine a value with the one of lane l ^ 16 (or l ^ 32), in every lane,
+// with the gfx950 lane swaps (one VALU op each, no LDS permute).  With both
+// operands x, element 0 + element 1 of v_permlane16_swap is x[l] + x[l ^ 16]
+// in every lane (likewise v_permlane32_swap for l ^ 32), the same two values
+// a __shfl_xor exchange adds.
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float x) { float a, b; swap16(x, a, b); return a + b; }
+__device__ __forceinline__ float sum_xor32(float x) { float a, b; swap32(x, a, b); return a + b; }
+__device__ __forceinline__ float max_xor16(float x) { float a, b; swap16(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float max_xor32(float x) { float a, b; swap32(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ uint32_t sum_xor16_u32(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return r[0] + r[1];
+}
+__device__ __forceinline__ uint32_t sum_xor32_u32(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return r[0] + r[1];
+}
+
 // Block-max reduction of key scores: NaN-propagating maximum (a block with a
 // NaN key scores NaN, like a maximum over the set taken in the plain
 // definition; ranked last).  On gfx950 it is v_maximum(3)_f32, with no

@@ -9,7 +9,8 @@
 // reads a fully contiguous 1 KB.  The lane's 8-dim slice of the query stays
 // in registers; partial dots (v_dot2_f32_bf16, fp32 accumulate of exact
 // bf16 products) are summed over the 16 lanes of a DPP row, the block max is
-// taken in-lane over k and across the four rows with two xor shuffles.
+// taken in-lane over k and across the four rows with two lane swaps
+// (v_permlane16_swap, v_permlane32_swap).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -50,8 +51,11 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerDecodeArgs a
       float m = -INFINITY;
 #pragma unroll
       for (int k = 0; k < 8; ++k) m = max_keep_nan(m, row16_sum(dot8_bf16(kv[k], qv)));
-      m = max_keep_nan(m, shfl_xor_f32(m, 16));
-      m = max_keep_nan(m, shfl_xor_f32(m, 32));
+      float a, b;
+      swap16(m, a, b);
+      m = max_keep_nan(a, b);
+      swap32(m, a, b);
+      m = max_keep_nan(a, b);
       score = m;
     }
     if (lane == 0) out[j] = score;

@@ -56,6 +56,23 @@ struct AttnArgs {
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 
+// Block-major prefill attention: the chunk's (row, slot) pairs bucketed by
+// block, one pass over each block's K/V tiles writing per-slot partials, a
+// log-sum-exp merge per (row, head).
+constexpr int32_t kMaxBlocksAttnBucket = 16384;  // bucket counts live in LDS
+struct PrefillAttnPlan {
+  int32_t max_chunks;  // upper bound of the number of row chunks
+  size_t off_off, choff_off, pairs_off, chunk_off, part_off;  // byte offsets in the workspace
+  size_t ws_bytes;     // 0: sizes not supported by this path
+};
+PrefillAttnPlan prefill_attn_plan(int32_t T, int32_t heads, int32_t topk, int32_t max_blocks);
+struct PrefillAttnArgs {
+  AttnArgs attn;  // prefill rows: nq = T
+  void* ws;
+  PrefillAttnPlan plan;
+};
+hipError_t launch_attn_prefill_blocks(const PrefillAttnArgs& a, hipStream_t stream);
+
 // Fused decode selection + attention (steps 3 and 4).
 constexpr int32_t kMaxFusedTopk = 256;
 constexpr int32_t kMaxFusedCandidates = 1024 * 16;

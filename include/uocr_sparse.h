@@ -259,6 +259,16 @@ int uocr_block_topk_prefill(const uocr_sparse_cfg* cfg, const void* cand_ws, siz
  * at p = q_start + t, all rows in sequence 0 of kv (kv->batch must be 1).
  *   q   : [T][H][D] bf16;  block_idx : [T][topk_blocks] int32
  *   out : [T][H][D] float32;  lse : [T][H] float32 or NULL
+ *   ws  : NULL, or a 256-byte aligned workspace of uocr_workspace_size(cfg,
+ *         UOCR_OP_ATTN_PREFILL, T, max_blocks) bytes.  With it, the chunk's
+ *         (row, slot) pairs are bucketed by block and each block's K/V tiles
+ *         are read once per chunk, each row's per-block partial softmax states
+ *         being merged afterwards (block-major); with ws NULL every row
+ *         gathers its own tiles (row-major).  Both give the same result up to
+ *         float32 summation order.  The size query returns 0 when this path
+ *         does not apply (max_blocks > 16384), and the row-major path then runs
+ *         whatever ws is.  UOCR_EWORKSPACE: ws non-NULL and too small;
+ *         UOCR_EINVAL: ws not 256-byte aligned.
  */
 int uocr_sparse_attn_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q, int32_t q_start,
                              int32_t T, const int32_t* block_idx, float* out, float* lse, void* ws,

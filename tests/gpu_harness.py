@@ -76,7 +76,9 @@ def gpu_attn_decode(dev, li: int, cfg, idx_np: np.ndarray):
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
-def gpu_prefill(dev, cfg, idx_override: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+def gpu_prefill(dev, cfg, idx_override: Optional[np.ndarray] = None, block_major: bool = True) -> Dict[str, np.ndarray]:
+    """Scoring, merge and attention of a prefill chunk; the attention runs
+    block-major (with its workspace) unless block_major is False."""
     wl = dev.wl
     T, M, H, D = wl.rows, wl.max_blocks, wl.heads, wl.head_dim
     topk = cfg.topk_blocks
@@ -92,7 +94,13 @@ def gpu_prefill(dev, cfg, idx_override: Optional[np.ndarray] = None) -> Dict[str
     U.indexer_score_prefill(cfg, kv, dev.q_idx, wl.q_start, T, wsarg)
     U.block_topk_prefill(cfg, wsarg, wl.q_start, T, M, idx, nsel)
     idx_in = idx if idx_override is None else torch.from_numpy(np.ascontiguousarray(idx_override, dtype=np.int32)).cuda()
-    U.sparse_attn_prefill(cfg, kv, dev.q, wl.q_start, T, idx_in, out, lse)
+    aws = None
+    if block_major:
+        ab = U.workspace_size(cfg, U.OP_ATTN_PREFILL, T, M)
+        assert ab > 0
+        aws = torch.empty(ab, dtype=torch.uint8, device="cuda")
+        aws.fill_(0x5A)  # stale contents must not matter
+    U.sparse_attn_prefill(cfg, kv, dev.q, wl.q_start, T, idx_in, out, lse, ws=aws)
     torch.cuda.synchronize()
     return {"idx": idx.cpu().numpy(), "nsel": nsel.cpu().numpy(), "out": out.cpu().numpy(),
             "lse": lse.cpu().numpy()}

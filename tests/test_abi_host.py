@@ -224,7 +224,11 @@ def test_prefill_argument_checks(U):
     need = U.workspace_size(cfg, U.OP_INDEXER_PREFILL, 100, 64)
     assert need > 0
     assert need == U.workspace_size(cfg, U.OP_TOPK_PREFILL, 100, 64)
-    assert U.workspace_size(cfg, U.OP_ATTN_PREFILL, 100, 64) == 0
+    attn_need = U.workspace_size(cfg, U.OP_ATTN_PREFILL, 100, 64)
+    # block-major prefill attention: one fp32 partial (o[128], m, l + pad) per (row, head, slot) and the buckets
+    assert attn_need >= 100 * 10 * 16 * 528 + 100 * 16 * 4
+    assert U.workspace_size(cfg, U.OP_ATTN_PREFILL, 200, 64) > attn_need
+    assert U.workspace_size(cfg, U.OP_ATTN_PREFILL, 100, 16385) == 0   # bucket counts must fit in LDS
     assert U.workspace_size(cfg, U.OP_ATTN_DECODE, 16, 4096) == 0
     with pytest.raises(U.UocrError) as e:
         U.indexer_score_prefill(cfg, _kv(U, batch=2, max_blocks=64), FAKE, 0, 100, (FAKE, need), stream=0)
@@ -251,6 +255,12 @@ def test_prefill_argument_checks(U):
     with pytest.raises(U.UocrError) as e:
         U.sparse_attn_prefill(cfg, kv1, FAKE, 2000, 100, FAKE, FAKE, stream=0)
     assert e.value.status == 2
+    with pytest.raises(U.UocrError) as e:   # block-major attention workspace too small
+        U.sparse_attn_prefill(cfg, kv1, FAKE, 0, 100, FAKE, FAKE, ws=(FAKE, attn_need - 1), stream=0)
+    assert e.value.status == 3
+    with pytest.raises(U.UocrError) as e:   # ... or not 256-byte aligned
+        U.sparse_attn_prefill(cfg, kv1, FAKE, 0, 100, FAKE, FAKE, ws=(FAKE + 16, attn_need), stream=0)
+    assert e.value.status == 1
     # T == 0 is a successful no-op
     U.indexer_score_prefill(cfg, kv1, None, 0, 0, None, stream=0)
     U.block_topk_prefill(cfg, None, 0, 0, 64, None, stream=0)

@@ -107,3 +107,49 @@ def test_prefill_nan_key_in_candidate_block_ranks_last():
         for j in nan_blocks:
             assert np.isnan(r["block_scores"][j])
             assert j not in r["selected"] and j not in res["idx"][t]
+
+
+def test_prefill_attention_block_major_matches_row_major_and_oracle():
+    """The block-major prefill attention (pairs bucketed by block, per-slot
+    partials, merge) against the row-major gather and the oracle, on index
+    sets that stress the bucketing: the rows' own selections, then random
+    sets with duplicates, -1 padding, out-of-range ids and blocks past p."""
+    wl = W.prefill_case("prefill attention paths S=4700 q_start=3000 T=1700", 0xF8, 4700, 3000, 1700)
+    print("case:", wl.name, flush=True)
+    cfg_u, cfg_o = G.cfg_for(wl), G.ocfg()
+    topk = cfg_u.topk_blocks
+    dev = SD.generate(wl)
+    res_b = G.gpu_prefill(dev, cfg_u)
+    res_r = G.gpu_prefill(dev, cfg_u, idx_override=res_b["idx"], block_major=False)
+    np.testing.assert_array_equal(res_b["idx"], res_r["idx"])
+    assert np.abs(res_b["out"] - res_r["out"]).max() <= 1e-5
+    assert np.abs(res_b["lse"] - res_r["lse"]).max() <= 1e-5
+
+    g = np.random.default_rng(0xF8)
+    T, M = wl.rows, wl.max_blocks
+    idx = np.full((T, topk), -1, np.int32)
+    for t in range(T):
+        nb = (wl.q_start + t) // 32 + 1
+        k = g.integers(0, topk + 1)
+        idx[t, :k] = g.integers(-3, nb + 6, size=k)   # some past p, some negative, some repeated
+    idx[5, :] = 7                                       # one block 16 times
+    idx[6, :] = M + 3                                   # all out of range: empty set
+    idx[7, :4] = [M - 1, M, 0, 0]
+    res_b = G.gpu_prefill(dev, cfg_u, idx_override=idx)
+    res_r = G.gpu_prefill(dev, cfg_u, idx_override=idx, block_major=False)
+    assert np.abs(res_b["out"] - res_r["out"]).max() <= 1e-5
+    fin = np.isfinite(res_r["lse"])
+    np.testing.assert_array_equal(fin, np.isfinite(res_b["lse"]))
+    assert np.abs(res_b["lse"][fin] - res_r["lse"][fin]).max() <= 1e-5
+    assert np.all(res_b["out"][6] == 0) and np.all(np.isneginf(res_b["lse"][6]))
+    allrows = np.arange(T)
+    q = wl.q_rows(allrows)
+    for t in list(range(0, T, 97)) + [5, 6, 7, T - 1]:
+        p = wl.q_start + t
+        sel = [int(j) for j in idx[t] if 0 <= j < M and j * 32 <= p]   # duplicates attend twice
+        if not sel:
+            continue
+        toks = np.concatenate([oracle.attended_tokens([j], p, cfg_o) for j in sel])
+        k_, v_ = G.fetcher(wl, 0, 0)(toks)
+        o2, l2 = oracle.attend(q[t], k_, v_, np.arange(toks.size), cfg_o.sm_scale)
+        G.check_attention(res_b["out"][t], res_b["lse"][t], o2, l2)
