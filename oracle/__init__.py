@@ -51,6 +51,7 @@ from .sr_swa import (  # noqa: F401
     prefill_rows_fetch,
 )
 from .page2d import (  # noqa: F401
+    page_coords,
     page2d_inv_freq,
     page2d_angles,
     rope_page2d_f64,

@@ -16,7 +16,17 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 * the main attention's q/k and the indexer's q/k share the coordinates; K
   is stored rotated in the cache.
 The rotation is exact in float64 and rounded once to bfloat16 (nearest, ties
-to even).  Coordinates are inputs.
+to even).
+
+Coordinates ([rkmt] Sec. 4, how positions are built and advanced): a page
+marker token opens a new page, so the page coordinate counts markers, and
+the token coordinate is the running count inside the current page.  In
+decoding, a {page, tok} state advances one token at a time: a marker adds one
+to page and sends tok back to the start of that page's segment; any other
+token adds one to tok.  Reading taken: the segment start is coordinate 0 and
+the marker is the first token of its page, so prefill of a stream and
+token-by-token decode are the same rule (``page_coords``), and prefill of a
+concatenation equals prefill of its first part followed by the rest.
 """
 from __future__ import annotations
 
@@ -28,6 +38,24 @@ TOK_THETA = 10000.0
 PAGE_THETA = 256.0
 PAGE_PAIRS = 1
 PAGE_MOD = 2
+
+
+def page_coords(tokens, marker: int, state=(0, -1)):
+    """(tok_pos, page_pos, state after) of a token stream from ``state`` =
+    (page, tok) of the token before it ([rkmt] Sec. 4): a marker token opens
+    page + 1 at tok 0; any other token is tok + 1 on the same page."""
+    page, tok = int(state[0]), int(state[1])
+    tok_pos = np.empty(len(tokens), np.int64)
+    page_pos = np.empty(len(tokens), np.int64)
+    for i, x in enumerate(tokens):
+        if int(x) == marker:
+            page += 1
+            tok = 0
+        else:
+            tok += 1
+        tok_pos[i] = tok
+        page_pos[i] = page
+    return tok_pos, page_pos, (page, tok)
 
 
 def page2d_inv_freq(head_dim: int = 128, tok_theta: float = TOK_THETA, page_theta: float = PAGE_THETA,

@@ -170,3 +170,95 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 
 def test_unmutated_page2d_passes_the_same_checks():
     assert _pins_pass()
+
+
+# ---------------------------------------------------------------- coordinates
+
+def _golden_coords():
+    d = {}
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "page_coords.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        k, *v = line.split()
+        d[k] = [int(x) for x in v]
+    return d
+
+
+def test_page_coords_golden_stream():
+    g = _golden_coords()
+    tp, pp, st = oracle.page_coords(g["tokens"], g["marker"][0], tuple(g["start"]))
+    assert list(tp) == g["tok"] and list(pp) == g["page"] and list(st) == g["after"]
+    tp2, pp2, st2 = oracle.page_coords(g["tokens2"], g["marker"][0], st)
+    assert list(tp2) == g["tok2"] and list(pp2) == g["page2"] and list(st2) == g["after2"]
+
+
+def _closed_form(tokens, marker, state):
+    """page = start page + markers so far; tok = distance to the last marker,
+    or the start tok + 1 + index before the first one."""
+    t = np.asarray(tokens)
+    is_m = t == marker
+    idx = np.arange(t.size)
+    last = np.maximum.accumulate(np.where(is_m, idx, -1)) if t.size else idx
+    page = state[0] + np.cumsum(is_m)
+    tok = np.where(last >= 0, idx - last, state[1] + 1 + idx)
+    return tok, page
+
+
+@pytest.mark.parametrize("density", [0.0, 0.01, 0.3, 1.0])
+def test_page_coords_closed_form_and_chunking(density):
+    g = np.random.default_rng(int(density * 1000) + 5)
+    marker = 9
+    toks = np.where(g.random(5000) < density, marker, g.integers(0, 9, 5000))
+    start = (int(g.integers(0, 50)), int(g.integers(-1, 300)))
+    tp, pp, st = oracle.page_coords(toks, marker, start)
+    ct, cp = _closed_form(toks, marker, start)
+    np.testing.assert_array_equal(tp, ct)
+    np.testing.assert_array_equal(pp, cp)
+    # prefill of the whole stream == chunked prefill == one-token decode steps
+    cuts = sorted(g.choice(np.arange(1, 5000), 7, replace=False))
+    s, parts_t, parts_p = start, [], []
+    for a, b in zip([0] + cuts, cuts + [5000]):
+        a_t, a_p, s = oracle.page_coords(toks[a:b], marker, s)
+        parts_t.append(a_t)
+        parts_p.append(a_p)
+    np.testing.assert_array_equal(np.concatenate(parts_t), tp)
+    np.testing.assert_array_equal(np.concatenate(parts_p), pp)
+    assert s == st
+    s2 = start
+    for x in toks[:300]:
+        (t1,), (p1,), s2 = oracle.page_coords([x], marker, s2)
+    assert (t1, p1) == (tp[299], pp[299])
+
+
+def test_page_coords_planted_mistakes():
+    g = _golden_coords()
+    m = g["marker"][0]
+
+    def no_reset(tokens, marker, state=(0, -1)):       # a marker advances tok instead of resetting it
+        page, tok = state
+        out_t, out_p = [], []
+        for x in tokens:
+            page += int(x == marker)
+            tok += 1
+            out_t.append(tok)
+            out_p.append(page)
+        return out_t, out_p, (page, tok)
+
+    def marker_on_old_page(tokens, marker, state=(0, -1)):   # the marker stays on the page it closes
+        page, tok = state
+        out_t, out_p = [], []
+        for x in tokens:
+            if x == marker:
+                out_t.append(0)
+                out_p.append(page)
+                page += 1
+                tok = 0
+            else:
+                tok += 1
+                out_t.append(tok)
+                out_p.append(page)
+        return out_t, out_p, (page, tok)
+
+    for mut in (no_reset, marker_on_old_page):
+        tp, pp, _ = mut(g["tokens"], m, tuple(g["start"]))
+        assert list(tp) != g["tok"] or list(pp) != g["page"], mut.__name__
