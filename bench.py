@@ -282,7 +282,8 @@ def run_page_gate(U, SD, W, torch, reps=20):
 
 
 def run_rope(U, torch, reps=20):
-    """page2d cache write + query rotation: one decode layer of 16 sequences
+    """page2d coordinates from the token stream (a page marker every 1000
+    tokens), cache write and query rotation: one decode layer of 16 sequences
     (one new token each) and one 2048-token prefill chunk, into block-major
     pools of 128K-token sequences; one event pair around back-to-back calls."""
     import numpy as np
@@ -301,10 +302,14 @@ def run_rope(U, torch, reps=20):
         table = torch.from_numpy(g.permutation(P).reshape(B, M).astype(np.int32)).cuda()
         ctx = torch.full((B,), M * 32, dtype=torch.int32, device="cuda")
         kv = U.make_kv(kp, vp, ip, table, ctx, P, B, M)
-        seq = torch.from_numpy((np.arange(n) % B).astype(np.int32)).cuda()
-        pos = torch.from_numpy((M * 32 - n // B + np.arange(n) // B).astype(np.int32)).cuda()
-        tok = torch.from_numpy((np.arange(n) % 1000).astype(np.int32)).cuda()
-        page = torch.from_numpy((np.arange(n) // 1000).astype(np.int32)).cuda()
+        per = n // B  # new tokens per sequence
+        seq = torch.from_numpy((np.arange(n) // per).astype(np.int32)).cuda()
+        pos = torch.from_numpy((M * 32 - per + np.arange(n) % per).astype(np.int32)).cuda()
+        marker = 151
+        stream_toks = torch.from_numpy(np.where(np.arange(n) % 1000 == 0, marker, 5).astype(np.int32)).cuda()
+        coord_state = torch.zeros((B, 2), dtype=torch.int32, device="cuda")
+        tok = torch.empty(n, dtype=torch.int32, device="cuda")
+        page = torch.empty(n, dtype=torch.int32, device="cuda")
         kn = torch.randn((n, H, D), device="cuda").to(torch.bfloat16).view(torch.int16)
         vn = torch.randn((n, H, D), device="cuda").to(torch.bfloat16).view(torch.int16)
         ixn = torch.randn((n, D), device="cuda").to(torch.bfloat16).view(torch.int16)
@@ -312,6 +317,7 @@ def run_rope(U, torch, reps=20):
         qi = torch.randn((n, D), device="cuda").to(torch.bfloat16).view(torch.int16)
 
         def call():
+            U.page_coords(B, per, stream_toks, marker, coord_state, tok, page, stream=sh)
             U.rope_cache_write(cfg, kv, n, seq, pos, tok, page, kn, vn, ixn, stream=sh)
             U.rope_queries(cfg, n, tok, page, q=q, q_idx=qi, stream=sh)
 
@@ -596,7 +602,7 @@ def main():
     if not args.no_rope:
         result["page2d_rope_cache_write"] = run_rope(U, torch)
         for k, v in result["page2d_rope_cache_write"].items():
-            log(f"page2d rope + cache write, {k}: {v['us']:.1f} us ({v['GBps']:.0f} GB/s)")
+            log(f"page2d coordinates + rope + cache write, {k}: {v['us']:.1f} us ({v['GBps']:.0f} GB/s)")
 
     print(json.dumps(result), flush=True)
 

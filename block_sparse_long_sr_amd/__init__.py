@@ -22,7 +22,7 @@ __all__ = [
     "workspace_size", "status_string", "last_error", "abi_version",
     "OP_INDEXER_DECODE", "OP_TOPK_DECODE", "OP_ATTN_DECODE",
     "OP_INDEXER_PREFILL", "OP_TOPK_PREFILL", "OP_ATTN_PREFILL", "OP_DENSE_ATTN_DECODE", "dense_attn_decode",
-    "rope_cache_write", "rope_queries",
+    "rope_cache_write", "rope_queries", "page_coords",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +93,7 @@ _SIGS = {
     "uocr_indexer_score_prefill": ([_CFG, _KV, _P, _I32, _I32, _P, _SZ, _P], ctypes.c_int),
     "uocr_block_topk_prefill": ([_CFG, _P, _SZ, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "uocr_sparse_attn_prefill": ([_CFG, _KV, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "uocr_page_coords": ([_I32, _I32, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
     "uocr_workspace_size": ([_CFG, _I32, _I32, _I32], ctypes.c_size_t),
     "uocr_status_string": ([_I32], ctypes.c_char_p),
     "uocr_last_error": ([], ctypes.c_char_p),
@@ -219,6 +220,11 @@ def sparse_attn_prefill(cfg: SparseCfg, kv: KV, q, q_start: int, T: int, block_i
     _check(_lib.uocr_sparse_attn_prefill(ctypes.byref(cfg), ctypes.byref(kv), _ptr(q), q_start, T, _ptr(block_idx),
                                          _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream)),
            "sparse_attn_prefill")
+
+
+def page_coords(batch: int, n: int, tokens, marker: int, state, tok_pos, page_pos, stream=None) -> None:
+    _check(_lib.uocr_page_coords(batch, n, _ptr(tokens), marker, _ptr(state), _ptr(tok_pos), _ptr(page_pos),
+                                 _stream(stream)), "page_coords")
 
 
 def workspace_size(cfg: SparseCfg, op: int, rows: int, max_blocks: int) -> int:

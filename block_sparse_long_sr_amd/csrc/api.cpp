@@ -436,6 +436,26 @@ int uocr_rope_queries(const uocr_sparse_cfg* cfg, int32_t n, const int32_t* tok_
   return hip_status(uocr::launch_rope_queries(a, static_cast<hipStream_t>(stream)), "rope_queries");
 }
 
+int uocr_page_coords(int32_t batch, int32_t n, const int32_t* tokens, int32_t marker, int32_t* state,
+                     int32_t* tok_pos, int32_t* page_pos, void* stream) {
+  if (batch < 0 || n < 0) return fail(UOCR_ESHAPE, "batch and n must be >= 0 (got %d, %d)", batch, n);
+  if (batch == 0 || n == 0) return ok();
+  if ((int64_t)batch * n > INT64_C(1) << 40) return fail(UOCR_ESHAPE, "batch * n too large");
+  REQ_PTR4(tokens, "tokens");
+  REQ_PTR4(state, "state");
+  REQ_PTR4(tok_pos, "tok_pos");
+  REQ_PTR4(page_pos, "page_pos");
+  uocr::PageCoordArgs a{};
+  a.tokens = tokens;
+  a.state = state;
+  a.tok_pos = tok_pos;
+  a.page_pos = page_pos;
+  a.batch = batch;
+  a.n = n;
+  a.marker = marker;
+  return hip_status(uocr::launch_page_coords(a, static_cast<hipStream_t>(stream)), "page_coords");
+}
+
 size_t uocr_workspace_size(const uocr_sparse_cfg* cfg, int32_t op, int32_t rows, int32_t max_blocks) {
   if (check_cfg(cfg) != UOCR_OK || rows < 0 || max_blocks < 1 || max_blocks > kMaxBlocks) return 0;
   switch (op) {

@@ -143,6 +143,19 @@ struct RopeQueryArgs {
 };
 hipError_t launch_rope_queries(const RopeQueryArgs& a, hipStream_t stream);
 
+// page2d coordinates of token streams: a page marker opens page + 1 at token
+// coordinate 0, any other token advances the in-page count.
+struct PageCoordArgs {
+  const int32_t* tokens;  // [batch][n]
+  int32_t* state;         // [batch][2]: page, tok of the token before; updated
+  int32_t* tok_pos;       // [batch][n]
+  int32_t* page_pos;      // [batch][n]
+  int32_t batch;
+  int32_t n;
+  int32_t marker;
+};
+hipError_t launch_page_coords(const PageCoordArgs& a, hipStream_t stream);
+
 // Chunked-prefill scoring: partition of the context into splits.
 struct PrefillPlan {
   int32_t n_tiles;   // ceil(T / 256) row tiles

@@ -122,4 +122,63 @@ hipError_t launch_rope_queries(const RopeQueryArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// page2d coordinates (news.rkmt.cn/news/25027 Sec. 4: the page coordinate
+// counts page markers, the token coordinate runs inside the page; decoding
+// advances a {page, tok} state per token, a marker moving to the next page
+// and sending tok back to the page's start).  One workgroup per sequence
+// scans its tokens in tiles of kCoordThreads: an inclusive scan of the marker
+// count and a max-scan of the last marker's position, carried across tiles;
+// the state after the last token is written back.
+namespace {
+constexpr int kCoordThreads = 256;
+}
+
+__global__ __launch_bounds__(kCoordThreads) void page_coords_kernel(PageCoordArgs a) {
+  __shared__ int32_t s_cnt[kCoordThreads];
+  __shared__ int32_t s_last[kCoordThreads];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t* tok_in = a.tokens + (int64_t)b * a.n;
+  int32_t page = a.state[2 * b];
+  int32_t tok = a.state[2 * b + 1];
+  for (int64_t base = 0; base < a.n; base += kCoordThreads) {
+    const int64_t i = base + tid;
+    const bool valid = i < a.n;
+    const bool mk = valid && tok_in[i] == a.marker;
+    s_cnt[tid] = mk ? 1 : 0;
+    s_last[tid] = mk ? tid : -1;
+    __syncthreads();
+    for (int d = 1; d < kCoordThreads; d <<= 1) {
+      const int c = tid >= d ? s_cnt[tid - d] : 0;
+      const int l = tid >= d ? s_last[tid - d] : -1;
+      __syncthreads();
+      s_cnt[tid] += c;
+      s_last[tid] = max(s_last[tid], l);
+      __syncthreads();
+    }
+    const int32_t my_page = page + s_cnt[tid];
+    const int32_t my_tok = s_last[tid] >= 0 ? tid - s_last[tid] : tok + 1 + tid;
+    if (valid) {
+      a.tok_pos[(int64_t)b * a.n + i] = my_tok;
+      a.page_pos[(int64_t)b * a.n + i] = my_page;
+    }
+    // carry: the state after the tile's last token
+    const int last = (int)min<int64_t>(kCoordThreads, a.n - base) - 1;
+    const int32_t c_last = s_cnt[last], l_last = s_last[last];
+    page += c_last;
+    tok = l_last >= 0 ? last - l_last : tok + 1 + last;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.state[2 * b] = page;
+    a.state[2 * b + 1] = tok;
+  }
+}
+
+hipError_t launch_page_coords(const PageCoordArgs& a, hipStream_t stream) {
+  if (a.batch == 0 || a.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(page_coords_kernel, dim3(a.batch), dim3(kCoordThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace uocr

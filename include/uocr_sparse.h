@@ -285,9 +285,8 @@ int uocr_sparse_attn_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, cons
  * (page_pos mod 2) * 256^0 for the page pair.  tok_pos is the token's offset
  * inside its page and page_pos its page number; the main attention's q/k and
  * the indexer's q/k share them.  The rotation is computed in float64 and
- * rounded once to bf16 (nearest, ties to even).  The coordinates are inputs:
- * the model's token bookkeeping (page markers) that produces them is not
- * part of this library.
+ * rounded once to bf16 (nearest, ties to even).  The coordinates are inputs
+ * here; uocr_page_coords derives them from the token stream.
  *
  * uocr_rope_cache_write stores n new tokens into the caches of kv: token t
  * of sequence seq[t] at position pos[t] gets its K rows (every head) and its
@@ -309,6 +308,24 @@ int uocr_rope_cache_write(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t
  */
 int uocr_rope_queries(const uocr_sparse_cfg* cfg, int32_t n, const int32_t* tok_pos, const int32_t* page_pos,
                       uint16_t* q, uint16_t* q_idx, void* stream);
+
+/*
+ * page2d coordinates of token streams (news.rkmt.cn/news/25027 Sec. 4: the
+ * page coordinate counts page markers and the token coordinate runs inside
+ * the page; in decoding a {page, tok} state advances per token, a marker
+ * moving to the next page and sending tok back to the page's start).  For
+ * each of `batch` streams of n tokens, from its state (page, tok of the token
+ * before the stream): a token equal to `marker` gets (tok 0, page + 1), any
+ * other token (tok + 1, page).  A prefill chunk is one stream (batch 1, n =
+ * chunk length); a decode step is batch sequences of one token each; calls
+ * carrying the state compose exactly like one call over the concatenation.
+ *   tokens            : [batch][n] int32
+ *   state             : [batch][2] int32 (page, tok), read and updated in place
+ *                       (start of a document: page 0, tok -1)
+ *   tok_pos, page_pos : [batch][n] int32, written
+ */
+int uocr_page_coords(int32_t batch, int32_t n, const int32_t* tokens, int32_t marker, int32_t* state,
+                     int32_t* tok_pos, int32_t* page_pos, void* stream);
 
 /* ------------------------------------------------------------- utilities */
 

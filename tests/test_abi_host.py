@@ -42,6 +42,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["uocr_indexer_score_decode", "uocr_block_topk_decode", "uocr_sparse_attn_decode",
               "uocr_topk_attn_decode", "uocr_dense_attn_decode", "uocr_rope_cache_write", "uocr_rope_queries",
+              "uocr_page_coords",
               "uocr_indexer_score_prefill", "uocr_block_topk_prefill", "uocr_sparse_attn_prefill",
               "uocr_workspace_size", "uocr_status_string", "uocr_last_error", "uocr_abi_version"]:
         assert n in names
@@ -187,6 +188,20 @@ def test_rope_argument_checks(U):
     assert e.value.status == 1 and "tok_pos" in U.last_error()
     U.rope_queries(cfg, 3, None, None, stream=0)                     # nothing to rotate
     U.rope_cache_write(cfg, _kv(U), 0, None, None, None, None, None, None, None, stream=0)
+
+
+def test_page_coords_argument_checks(U):
+    with pytest.raises(U.UocrError) as e:
+        U.page_coords(2, -1, FAKE, 7, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(U.UocrError) as e:
+        U.page_coords(2, 5, FAKE, 7, None, FAKE, FAKE, stream=0)
+    assert e.value.status == 1 and "state" in U.last_error()
+    with pytest.raises(U.UocrError) as e:
+        U.page_coords(2, 5, FAKE, 7, FAKE, FAKE + 2, FAKE, stream=0)   # misaligned int32 array
+    assert e.value.status == 1 and "tok_pos" in U.last_error()
+    U.page_coords(0, 5, None, 7, None, None, None, stream=0)          # empty: no-op
+    U.page_coords(3, 0, None, 7, None, None, None, stream=0)
 
 
 def test_page_tags_need_query_pages(U):

@@ -119,3 +119,66 @@ def test_decode_on_caches_written_by_the_rope_kernel():
     got = [int(x) for x in idx.cpu().numpy()[0] if x >= 0]
     if got == ref["selected"]:
         G.check_attention(out.cpu().numpy()[0], lse.cpu().numpy()[0], ref["out"], ref["lse"])
+
+
+def test_page_coords_prefill_chunks_and_decode_steps_bit_exact():
+    """uocr_page_coords against the oracle's coordinate rule: several
+    streams over several 256-token tiles with ragged tails, chunked calls
+    carrying the state, and one-token decode steps of a batch."""
+    g = np.random.default_rng(0xC0)
+    marker = 151
+    B, n = 5, 1000
+    dens = [0.0, 0.002, 0.05, 0.5, 1.0]
+    toks = np.stack([np.where(g.random(n) < d, marker, g.integers(0, 150, n)) for d in dens]).astype(np.int32)
+    start = np.stack([g.integers(0, 20, B), g.integers(-1, 500, B)], axis=1).astype(np.int32)
+    keep = []
+
+    def run(tk, st):
+        tk = np.ascontiguousarray(tk, dtype=np.int32)
+        bb, nn = tk.shape
+        d_tok, d_st = _dev(tk), _dev(st.astype(np.int32))
+        d_tp = torch.full((bb, nn), -7, dtype=torch.int32, device="cuda")
+        d_pp = torch.full((bb, nn), -7, dtype=torch.int32, device="cuda")
+        keep.extend([d_tok, d_st, d_tp, d_pp])
+        U.page_coords(bb, nn, d_tok, marker, d_st, d_tp, d_pp)
+        torch.cuda.synchronize()
+        return d_tp.cpu().numpy(), d_pp.cpu().numpy(), d_st.cpu().numpy()
+
+    tp, pp, st = run(toks, start)
+    for b in range(B):
+        ot, op, os_ = oracle.page_coords(toks[b], marker, tuple(start[b]))
+        np.testing.assert_array_equal(tp[b], ot)
+        np.testing.assert_array_equal(pp[b], op)
+        assert tuple(st[b]) == os_
+    # one stream in chunks of 1, 255, 256, 257 and the rest, state carried on the device
+    s = start[3:4].copy()
+    out_t, out_p = [], []
+    a = 0
+    for c in [1, 255, 256, 257, n - 769]:
+        t_, p_, s = run(toks[3:4, a:a + c], s)
+        out_t.append(t_[0])
+        out_p.append(p_[0])
+        a += c
+    np.testing.assert_array_equal(np.concatenate(out_t), tp[3])
+    np.testing.assert_array_equal(np.concatenate(out_p), pp[3])
+    # decode: 16 sequences, 300 steps of one token each
+    D, steps = 16, 300
+    dt = np.where(g.random((D, steps)) < 0.03, marker, g.integers(0, 150, (D, steps))).astype(np.int32)
+    ds = np.stack([np.zeros(D), np.full(D, -1)], axis=1).astype(np.int32)
+    d_st = _dev(ds)
+    got_t = np.empty((D, steps), np.int64)
+    got_p = np.empty((D, steps), np.int64)
+    d_tp = torch.empty((D, 1), dtype=torch.int32, device="cuda")
+    d_pp = torch.empty((D, 1), dtype=torch.int32, device="cuda")
+    d_all = _dev(np.ascontiguousarray(dt.T))          # [steps][D]
+    for k in range(steps):
+        U.page_coords(D, 1, d_all[k], marker, d_st, d_tp, d_pp)
+        if k % 50 == 49 or k == steps - 1:
+            torch.cuda.synchronize()
+        got_t[:, k] = d_tp[:, 0].cpu().numpy()
+        got_p[:, k] = d_pp[:, 0].cpu().numpy()
+    for b in range(D):
+        ot, op, os_ = oracle.page_coords(dt[b], marker, (0, -1))
+        np.testing.assert_array_equal(got_t[b], ot)
+        np.testing.assert_array_equal(got_p[b], op)
+        assert tuple(d_st.cpu().numpy()[b]) == os_
