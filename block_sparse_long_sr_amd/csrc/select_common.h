@@ -170,23 +170,24 @@ __device__ __forceinline__ void select_sorted_reg(const float* sc, int ncand, in
   }
   __syncthreads();
   {
-    uint32_t pending = 0;
+    static_assert(KPT <= 64, "pending holds one bit per key of the thread");
+    uint64_t pending = 0;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) pending |= (tid + i * NT < ncand) ? (1u << i) : 0u;
+    for (int i = 0; i < KPT; ++i) pending |= (tid + i * NT < ncand) ? (1ull << i) : 0ull;
     while (__ballot(pending != 0) != 0) {
       const uint64_t act = __ballot(pending != 0);
       const int leader = __builtin_ctzll(act);
       uint32_t first = 0;
 #pragma unroll
       for (int i = KPT - 1; i >= 0; --i)
-        if (pending & (1u << i)) first = key[i] >> 24;
+        if (pending & (1ull << i)) first = key[i] >> 24;
       const uint32_t d = __builtin_amdgcn_readlane(first, leader);
       uint32_t cnt = 0;
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
-        const bool hit = (pending & (1u << i)) && (key[i] >> 24) == d;
+        const bool hit = (pending & (1ull << i)) && (key[i] >> 24) == d;
         cnt += hit ? 1u : 0u;
-        pending &= hit ? ~(1u << i) : ~0u;
+        pending &= hit ? ~(1ull << i) : ~0ull;
       }
       cnt = wave_sum_u32(cnt);
       if (lane == 0) atomicAdd(&hist[d], cnt);
