@@ -21,14 +21,16 @@ Sources (cited by short name in the docstrings):
            1.77 GB), Sec. 2 route A (Page Gate, Token Sieve, Local Window)
            and Sec. 3 (the chunked-prefill [tokens, context/32] temporary).
 
-Modules: ``sr_swa`` (steps 1-4 of the attention, the page-aware ranking)
-and ``page2d`` (the page2d rotary encoding and the cache write, [rkmt]
-Sec. 4).
+Modules: ``sr_swa`` (steps 1-4 of the attention, the page-aware ranking),
+``page2d`` (the page2d rotary encoding and the cache write, [rkmt]
+Sec. 4) and ``page_window`` (the page-window schedule of continuous
+decoding, [lehvn] Sec. 2 route A, storage half).
 
 Where the pages leave a step open, the reading taken is stated at the
 function that implements it.
 
-Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_oracle_page2d.py`` and ``tests/test_oracle_page_window.py``
 (brute force, dense-attention special cases, invariants, exact integer
 cases, golden fixtures).  None is "parity unpinned".
 """
@@ -59,3 +61,4 @@ from .page2d import (  # noqa: F401
     bf16_bits_nearest,
     cache_write,
 )
+from .page_window import page_window_schedule  # noqa: F401
