@@ -337,6 +337,32 @@ def run_rope(U, torch, reps=20):
     return res
 
 
+def run_page_window(U):
+    """Peak KV of the page-window schedule (host block pool, no GPU work):
+    documents of 400 image + 600 text tokens per page, windows of 10 pages,
+    the last 128 text tokens kept across a boundary, against keeping every
+    block; bytes for 12 layers of K, V (10 heads x 128, bf16) and indexer K
+    (128, bf16) per token slot."""
+    import time
+
+    slot_bytes = 12 * (2 * 10 * 128 * 2 + 128 * 2)   # 64512 B per token slot, all layers
+    W, tail, img, txt = 10, 128, 400, 600
+    res = {"window_pages": W, "text_tail_tokens": tail, "page_tokens": {"image": img, "text": txt},
+           "bytes_per_token_slot": slot_bytes, "documents": {}}
+    for pages in (100, 1000):
+        pool = U.BlockPool(1 << 20)
+        t0 = time.perf_counter()
+        peaks = pool.page_window_run(0, [img] * pages, [txt] * pages, W, tail)
+        host_us = (time.perf_counter() - t0) * 1e6
+        full_blocks = -(-pages * (img + txt) // 32)
+        res["documents"][f"{pages} pages"] = {
+            "windows": len(peaks), "peak_blocks": pool.peak, "peak_GB": pool.peak * 32 * slot_bytes / 1e9,
+            "no_eviction_blocks": full_blocks, "no_eviction_GB": full_blocks * 32 * slot_bytes / 1e9,
+            "host_us": host_us}
+        pool.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -603,6 +629,11 @@ def main():
         result["page2d_rope_cache_write"] = run_rope(U, torch)
         for k, v in result["page2d_rope_cache_write"].items():
             log(f"page2d coordinates + rope + cache write, {k}: {v['us']:.1f} us ({v['GBps']:.0f} GB/s)")
+
+    result["page_window_kv"] = run_page_window(U)
+    for k, v in result["page_window_kv"]["documents"].items():
+        log(f"page-window schedule, {k}: peak KV {v['peak_GB']:.2f} GB ({v['peak_blocks']} blocks), "
+            f"{v['no_eviction_GB']:.2f} GB without eviction")
 
     print(json.dumps(result), flush=True)
 

@@ -22,7 +22,7 @@ __all__ = [
     "workspace_size", "status_string", "last_error", "abi_version",
     "OP_INDEXER_DECODE", "OP_TOPK_DECODE", "OP_ATTN_DECODE",
     "OP_INDEXER_PREFILL", "OP_TOPK_PREFILL", "OP_ATTN_PREFILL", "OP_DENSE_ATTN_DECODE", "dense_attn_decode",
-    "rope_cache_write", "rope_queries", "page_coords",
+    "rope_cache_write", "rope_queries", "page_coords", "BlockPool", "PageWindow",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +62,10 @@ class KV(ctypes.Structure):
     ]
 
 
+class PageWindow(ctypes.Structure):
+    _fields_ = [("window_pages", ctypes.c_int32), ("text_tail_tokens", ctypes.c_int32)]
+
+
 class UocrError(RuntimeError):
     def __init__(self, status: int, func: str):
         self.status = status
@@ -94,6 +98,14 @@ _SIGS = {
     "uocr_block_topk_prefill": ([_CFG, _P, _SZ, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "uocr_sparse_attn_prefill": ([_CFG, _KV, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "uocr_page_coords": ([_I32, _I32, _P, _I32, _P, _P, _P, _P], ctypes.c_int),
+    "uocr_pool_create": ([_I32, _I32], _P),
+    "uocr_pool_destroy": ([_P], None),
+    "uocr_pool_append": ([_P, _I32, ctypes.c_int64], ctypes.c_int),
+    "uocr_pool_keep": ([_P, _I32, _P, _I32], ctypes.c_int),
+    "uocr_pool_table": ([_P, _I32, _P, _I32, _P], ctypes.c_int),
+    "uocr_pool_used": ([_P], ctypes.c_int64),
+    "uocr_pool_peak": ([_P], ctypes.c_int64),
+    "uocr_page_window_run": ([ctypes.POINTER(PageWindow), _P, _P, _I32, _P, _I32, _P, _I32], ctypes.c_int),
     "uocr_workspace_size": ([_CFG, _I32, _I32, _I32], ctypes.c_size_t),
     "uocr_status_string": ([_I32], ctypes.c_char_p),
     "uocr_last_error": ([], ctypes.c_char_p),
@@ -225,6 +237,63 @@ def sparse_attn_prefill(cfg: SparseCfg, kv: KV, q, q_start: int, T: int, block_i
 def page_coords(batch: int, n: int, tokens, marker: int, state, tok_pos, page_pos, stream=None) -> None:
     _check(_lib.uocr_page_coords(batch, n, _ptr(tokens), marker, _ptr(state), _ptr(tok_pos), _ptr(page_pos),
                                  _stream(stream)), "page_coords")
+
+
+class BlockPool:
+    """Host-side block pool of the paged caches (no GPU calls).
+
+    Owns one ``uocr_pool``; ``table`` returns a sequence's block-table row
+    and length, ready to upload as ``block_table`` / ``ctx_lens``.
+    """
+
+    def __init__(self, num_blocks: int, max_seqs: int = 1):
+        self._h = _lib.uocr_pool_create(int(num_blocks), int(max_seqs))
+        if not self._h:
+            raise ValueError(f"uocr_pool_create: {last_error()}")
+
+    def close(self) -> None:
+        if self._h:
+            _lib.uocr_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def append(self, seq: int, n_tokens: int) -> None:
+        _check(_lib.uocr_pool_append(self._h, int(seq), int(n_tokens)), "pool_append")
+
+    def keep(self, seq: int, ranges) -> None:
+        flat = (ctypes.c_int64 * (2 * len(ranges)))(*[int(v) for r in ranges for v in r])
+        _check(_lib.uocr_pool_keep(self._h, int(seq), flat, len(ranges)), "pool_keep")
+
+    def table(self, seq: int, max_blocks: int):
+        row = (ctypes.c_int32 * max(int(max_blocks), 1))()
+        length = ctypes.c_int64()
+        _check(_lib.uocr_pool_table(self._h, int(seq), row, int(max_blocks), ctypes.byref(length)), "pool_table")
+        return list(row)[:int(max_blocks)], int(length.value)
+
+    @property
+    def used(self) -> int:
+        return int(_lib.uocr_pool_used(self._h))
+
+    @property
+    def peak(self) -> int:
+        return int(_lib.uocr_pool_peak(self._h))
+
+    def page_window_run(self, seq: int, image_tokens, text_tokens, window_pages: int, text_tail_tokens: int):
+        """Run a document through the page-window schedule; returns the
+        per-window peak block counts."""
+        n = len(image_tokens)
+        if len(text_tokens) != n:
+            raise ValueError("image_tokens and text_tokens need one entry per page")
+        img = (ctypes.c_int32 * max(n, 1))(*[int(v) for v in image_tokens])
+        txt = (ctypes.c_int32 * max(n, 1))(*[int(v) for v in text_tokens])
+        peaks = (ctypes.c_int64 * max(n, 1))()
+        cfg = PageWindow(int(window_pages), int(text_tail_tokens))
+        _check(_lib.uocr_page_window_run(ctypes.byref(cfg), img, txt, n, self._h, int(seq), peaks, n),
+               "page_window_run")
+        n_windows = n if n <= 1 else 1 + (n - 2) // (int(window_pages) - 1)
+        return [int(v) for v in peaks[:n_windows]]
 
 
 def workspace_size(cfg: SparseCfg, op: int, rows: int, max_blocks: int) -> int:

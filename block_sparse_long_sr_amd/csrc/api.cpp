@@ -28,6 +28,26 @@ int ok() {
   return UOCR_OK;
 }
 
+}  // namespace
+
+namespace uocr {
+// Status and error text for the host-only parts of the library (pool.cpp):
+// UOCR_OK clears the text.
+int set_error(int status, const char* fmt, ...) {
+  if (status == UOCR_OK) {
+    g_last_error[0] = '\0';
+    return UOCR_OK;
+  }
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+}  // namespace uocr
+
+namespace {
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
@@ -480,6 +500,7 @@ const char* uocr_status_string(int32_t status) {
     case UOCR_EWORKSPACE: return "UOCR_EWORKSPACE: workspace missing or too small";
     case UOCR_EHIP: return "UOCR_EHIP: HIP launch error";
     case UOCR_EUNSUPPORTED: return "UOCR_EUNSUPPORTED: configuration not supported";
+    case UOCR_ECAPACITY: return "UOCR_ECAPACITY: block pool exhausted";
     default: return "unknown status";
   }
 }

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define UOCR_ABI_VERSION 2
+#define UOCR_ABI_VERSION 3
 
 /* Status codes. */
 enum {
@@ -54,7 +54,8 @@ enum {
   UOCR_ESHAPE = 2,      /* sizes or offsets out of the supported range          */
   UOCR_EWORKSPACE = 3,  /* workspace missing or smaller than required           */
   UOCR_EHIP = 4,        /* a HIP launch reported an error                       */
-  UOCR_EUNSUPPORTED = 5 /* valid but not supported by this build (see fields)   */
+  UOCR_EUNSUPPORTED = 5, /* valid but not supported by this build (see fields)  */
+  UOCR_ECAPACITY = 6     /* the block pool has too few free blocks              */
 };
 
 /* Operation ids for uocr_workspace_size(). */
@@ -326,6 +327,69 @@ int uocr_rope_queries(const uocr_sparse_cfg* cfg, int32_t n, const int32_t* tok_
  */
 int uocr_page_coords(int32_t batch, int32_t n, const int32_t* tokens, int32_t marker, int32_t* state,
                      int32_t* tok_pos, int32_t* page_pos, void* stream);
+
+/* ------------------------------------- block pool and page-window schedule */
+
+/*
+ * Host-side block pool of the paged caches: it hands out the physical block
+ * ids that block_table rows hold (a block = 32 token slots of the K, V and
+ * indexer-K pools).  K is stored already rotated with page-local
+ * coordinates, so kept blocks can be renumbered: releasing part of a
+ * sequence and compacting its table moves no cache data.  Not thread-safe;
+ * no GPU calls.
+ *
+ * uocr_pool_create: num_blocks physical blocks (ids 0..num_blocks-1), up to
+ *   max_seqs sequences, all empty; NULL on bad sizes (uocr_last_error says
+ *   why).  Free ids are handed out lowest first.
+ * uocr_pool_append: grow sequence seq by n_tokens, taking blocks as the
+ *   length crosses 32-token boundaries; UOCR_ECAPACITY (nothing changed) when
+ *   too few blocks are free.
+ * uocr_pool_keep: keep only the blocks that cover the token ranges
+ *   [ranges[2r], ranges[2r+1]) (ascending, inside the sequence), in order,
+ *   and release the others; the kept blocks become logical blocks 0, 1, ...
+ *   and the length becomes 32 per kept block, except that a kept last block
+ *   keeps its fill.  The tokens of kept blocks are all kept (ranges are
+ *   rounded out to whole blocks).  Bad ranges give UOCR_ESHAPE and change
+ *   nothing.
+ * uocr_pool_table: the sequence's block-table row (-1 padded to max_blocks
+ *   entries) and its length in tokens, for upload as block_table / ctx_lens.
+ * uocr_pool_used / uocr_pool_peak: blocks in use now / at most since creation
+ *   (-1 for a NULL pool).
+ */
+typedef struct uocr_pool uocr_pool;
+uocr_pool* uocr_pool_create(int32_t num_blocks, int32_t max_seqs);
+void uocr_pool_destroy(uocr_pool* pool);
+int uocr_pool_append(uocr_pool* pool, int32_t seq, int64_t n_tokens);
+int uocr_pool_keep(uocr_pool* pool, int32_t seq, const int64_t* ranges, int32_t n_ranges);
+int uocr_pool_table(const uocr_pool* pool, int32_t seq, int32_t* table, int32_t max_blocks, int64_t* length);
+int64_t uocr_pool_used(const uocr_pool* pool);
+int64_t uocr_pool_peak(const uocr_pool* pool);
+
+/*
+ * Page-window schedule of continuous decoding (leheavengame.com OCR 2
+ * release article, Sec. 2: parse the document in page windows, adjacent
+ * windows sharing one page; on entering the next window keep that page's
+ * visual KV and the text at the end of the previous window, release the
+ * rest; Sec. 3: the serving deployment's base window of 10 pages).
+ * Runs a document of n_pages pages (page k: image_tokens[k] visual tokens,
+ * text_tokens[k] parsed-text tokens) through empty sequence seq of pool:
+ * window w covers pages w(W-1) .. w(W-1)+W-1 (W = window_pages >= 2); it
+ * appends the visual tokens of its pages (all but the shared first page
+ * when w > 0), then their text; before the next window, uocr_pool_keep
+ * keeps the visual tokens of the window's last page and its last
+ * text_tail_tokens text tokens.  window_peaks[w] (if not NULL; max_windows
+ * entries) gets the most blocks in use during window w.  Errors: UOCR_EINVAL
+ * for NULL arguments, UOCR_ESHAPE for a bad config, a non-empty sequence,
+ * negative page sizes or too small a window_peaks (all checked before any
+ * change), UOCR_ECAPACITY when the pool runs out part-way (the sequence then
+ * holds what the schedule had reached).
+ */
+typedef struct uocr_page_window {
+  int32_t window_pages;
+  int32_t text_tail_tokens;
+} uocr_page_window;
+int uocr_page_window_run(const uocr_page_window* cfg, const int32_t* image_tokens, const int32_t* text_tokens,
+                         int32_t n_pages, uocr_pool* pool, int32_t seq, int64_t* window_peaks, int32_t max_windows);
 
 /* ------------------------------------------------------------- utilities */
 

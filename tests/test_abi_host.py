@@ -42,7 +42,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["uocr_indexer_score_decode", "uocr_block_topk_decode", "uocr_sparse_attn_decode",
               "uocr_topk_attn_decode", "uocr_dense_attn_decode", "uocr_rope_cache_write", "uocr_rope_queries",
-              "uocr_page_coords",
+              "uocr_page_coords", "uocr_pool_create", "uocr_pool_destroy", "uocr_pool_append", "uocr_pool_keep",
+              "uocr_pool_table", "uocr_pool_used", "uocr_pool_peak", "uocr_page_window_run",
               "uocr_indexer_score_prefill", "uocr_block_topk_prefill", "uocr_sparse_attn_prefill",
               "uocr_workspace_size", "uocr_status_string", "uocr_last_error", "uocr_abi_version"]:
         assert n in names
@@ -58,7 +59,8 @@ def test_struct_layouts_match_header(U, tmp_path):
     """The binding's ctypes mirrors have the sizes and field offsets that a C
     compiler gives the header's structs."""
     import subprocess
-    fields = {"uocr_sparse_cfg": [f for f, _ in U.SparseCfg._fields_], "uocr_kv": [f for f, _ in U.KV._fields_]}
+    mirrors = (("uocr_sparse_cfg", U.SparseCfg), ("uocr_kv", U.KV), ("uocr_page_window", U.PageWindow))
+    fields = {st: [f for f, _ in cls._fields_] for st, cls in mirrors}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "uocr_sparse.h"', "int main(void) {"]
     for st, fs in fields.items():
         lines.append(f'  printf("{st} %zu\\n", sizeof({st}));')
@@ -71,17 +73,18 @@ def test_struct_layouts_match_header(U, tmp_path):
     subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = dict(l.split() for l in subprocess.run([str(exe)], check=True, capture_output=True,
                                                  text=True).stdout.splitlines())
-    for st, cls in (("uocr_sparse_cfg", U.SparseCfg), ("uocr_kv", U.KV)):
+    for st, cls in mirrors:
         assert int(got[st]) == ctypes.sizeof(cls)
         for f in fields[st]:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, f
-    assert int(got["abi"]) == U.abi_version() == 2
+    assert int(got["abi"]) == U.abi_version() == 3
 
 
 def test_status_strings(U):
     assert U.status_string(0) == "UOCR_OK"
-    for c in range(1, 6):
+    for c in range(1, 7):
         assert U.status_string(c).startswith("UOCR_E")
+    assert U.status_string(6).startswith("UOCR_ECAPACITY")
 
 
 FAKE = 0x10000  # a 16-byte aligned fake device address; never dereferenced
