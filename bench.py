@@ -3,13 +3,16 @@
 Workload (the headline case): decode batch of 16 sequences x 12 layers at
 S = 131072 tokens (4096 blocks of 32), 10 heads x 128 bf16 K/V, 1 x 128
 indexer, 12 planted blocks per query, all resident in HBM (~135 GB).  One
-step = for each of the 12 layers, in order: indexer score + block max, top-k
-block selection, sparse attention -- the three decode entry points of the C
-ABI, 36 stream-ordered launches.  ``value`` is decode query-heads/s
-(16 * 12 * 10 per step).
+step = for each of the 12 layers of each sequence, in layer order: indexer
+score + block max, top-k block selection, sparse attention.  By default the
+step is one uocr_sparse_decode_step launch (work items in ticket order,
+layer l + 1 of a sequence after its layer l); --multi-launch runs it as
+per-layer launches of the separate entry points on micro-batch streams.
+``value`` is decode query-heads/s (16 * 12 * 10 per step).
 
-The same JSON line carries the roofline of the dominant kernel (the decode
-indexer, HBM bound) timed with HIP events, the CPU oracle's throughput on a
+The same JSON line carries the roofline of the dominant kernel (the
+one-launch step kernel, HBM bound, or the decode indexer with
+--multi-launch) timed with HIP events, the CPU oracle's throughput on a
 bounded sample of the same workload, and the chunked-prefill case
 (2048 rows at offset 129024 of a 131072-token context) with the MFMA
 roofline of its scoring kernel.
@@ -32,7 +35,13 @@ METRIC = "sparse-attn decode query-heads/s at 128K ctx; achieved HBM GB/s vs pea
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 KERNEL_SOURCES = {
+    "decode_step": ["block_sparse_long_sr_amd/csrc/decode_step.hip",
+                    "block_sparse_long_sr_amd/csrc/indexer_common.h",
+                    "block_sparse_long_sr_amd/csrc/attn_common.h",
+                    "block_sparse_long_sr_amd/csrc/select_common.h",
+                    "block_sparse_long_sr_amd/csrc/device_common.h"],
     "indexer_decode": ["block_sparse_long_sr_amd/csrc/indexer_decode.hip",
+                       "block_sparse_long_sr_amd/csrc/indexer_common.h",
                        "block_sparse_long_sr_amd/csrc/device_common.h"],
     "indexer_prefill": ["block_sparse_long_sr_amd/csrc/indexer_prefill.hip",
                         "block_sparse_long_sr_amd/csrc/device_common.h"],
@@ -69,7 +78,8 @@ def decode_bytes(wl, cfg_topk=16, local=4, heads=10, D=128, Di=128):
     return idx_b, topk_b, attn_b
 
 
-TRAFFIC_FILES = {"indexer_decode": "profiles/indexer_score_decode_128k_traffic.txt",
+TRAFFIC_FILES = {"decode_step": "profiles/decode_step_128k_traffic.txt",
+                 "indexer_decode": "profiles/indexer_score_decode_128k_traffic.txt",
                  "indexer_prefill": "profiles/indexer_score_prefill_2048_traffic.txt"}
 
 
@@ -369,7 +379,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--graph", action="store_true",
-                    help="capture one decode step as a HIP graph and time its replays")
+                    help="with --multi-launch: capture one decode step as a HIP graph and time its replays")
+    ap.add_argument("--multi-launch", action="store_true",
+                    help="run the step as per-layer launches (indexer, then selection + attention) on micro-batch "
+                         "streams instead of the one uocr_sparse_decode_step launch")
     ap.add_argument("--separate", action="store_true",
                     help="run selection and attention as two launches instead of the fused one")
     ap.add_argument("--streams", type=int, default=2,
@@ -446,7 +459,17 @@ def main():
                                  wl.pool_blocks, b1 - b0, M))
         groups.append((b0, b1, gkv, torch.cuda.Stream() if ns > 1 or args.graph else stream))
 
+    one_launch = not args.multi_launch
+    step_ws = None
+    if one_launch:
+        wsb = U.workspace_size(cfg, U.OP_DECODE_STEP, L * B, M)
+        step_ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        kv0 = dev.kv(0)
+
     def step():
+        if one_launch:
+            U.sparse_decode_step(cfg, kv0, L, dev.q_idx, dev.q, scores, idx, out, lse, ws=step_ws, stream=sh)
+            return
         for l in range(L):
             for b0, b1, gkv, st in groups:
                 h_ = st.cuda_stream
@@ -480,7 +503,7 @@ def main():
     join(stream)
     torch.cuda.synchronize()
     graph = None
-    if args.graph:
+    if args.graph and not one_launch:
         # One step (12 layers of every micro-batch group) captured as a HIP
         # graph; each replay relaunches all of its kernels on the same inputs.
         graph = torch.cuda.CUDAGraph()
@@ -508,6 +531,8 @@ def main():
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / args.steps
+    if step_ws is not None and int(step_ws[4:8].cpu().numpy().view(np.uint32)[0]) != 0:
+        raise RuntimeError("a dependency wait of the one-launch decode step gave up")
     qh_per_s = B * L * H * args.steps / (ms_total * 1e-3)
     log(f"decode step {ms_step * 1e3:.1f} us, {qh_per_s / 1e6:.3f} M query-heads/s")
 
@@ -529,6 +554,19 @@ def main():
         torch.cuda.synchronize()
         return sum(a_.elapsed_time(b_) for a_, b_ in pairs) / (len(pairs) * L)
 
+    t_step_kernel = None
+    if one_launch:
+        # the one-launch step timed alone, back to back on one stream: its
+        # main kernel plus the tiny counter-clearing kernel before it
+        pairs = []
+        for _ in range(ksteps):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            step()
+            b_.record(stream)
+            pairs.append((a_, b_))
+        torch.cuda.synchronize()
+        t_step_kernel = sum(a_.elapsed_time(b_) for a_, b_ in pairs) / len(pairs)
     t_idx = timed(lambda l: U.indexer_score_decode(cfg, kvs[l], dev.q_idx[l], scores[l], stream=sh))
     t_topk = timed(lambda l: U.block_topk_decode(cfg, scores[l], dev.ctx_lens, B, M, idx[l], stream=sh))
     t_attn = timed(lambda l: U.sparse_attn_decode(cfg, kvs[l], dev.q[l], idx[l], out[l], lse[l], stream=sh))
@@ -555,20 +593,36 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "layers": L, "ctx_len": int(wl.ctx_lens[0]),
                    "heads": H, "head_dim": 128, "block_size": 32, "topk_blocks": 16, "local_blocks": 4,
-                   "queries_per_step": B * L, "plant": wl.notes, "micro_batches": ns, "hip_graph": bool(args.graph)},
+                   "queries_per_step": B * L, "plant": wl.notes,
+                   "launches": "one uocr_sparse_decode_step per step" if one_launch else
+                               f"per layer, {ns} micro-batch streams" + (", HIP graph" if args.graph else "")},
         "tokens_per_s": B / (ms_step * 1e-3),
         "step_hbm_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "step_algorithmic_bytes": step_bytes,
         "kernel_us": {"indexer_score_decode": t_idx * 1e3, "block_topk_decode": t_topk * 1e3,
                       "sparse_attn_decode": t_attn * 1e3, "topk_attn_decode": t_fused * 1e3},
-        "step_launches": "indexer_score_decode + " + ("block_topk_decode + sparse_attn_decode" if args.separate
-                                                      else "topk_attn_decode") + " per layer",
-        "roofline": {"kernel": "indexer_score_decode", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "algorithmic_bytes_per_launch": idx_bytes,
-                     "traffic": traffic_for("indexer_decode")},
+        "step_launches": ("decode_step_clear_kernel + decode_step_kernel" if one_launch else
+                          "indexer_score_decode + " + ("block_topk_decode + sparse_attn_decode" if args.separate
+                                                       else "topk_attn_decode") + " per layer"),
     }
+    if one_launch:
+        step_achieved = step_bytes / (t_step_kernel * 1e-3) / 1e9
+        result["kernel_us"]["sparse_decode_step"] = t_step_kernel * 1e3
+        result["roofline"] = {"kernel": "decode_step_kernel", "bound": "hbm", "achieved": step_achieved,
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": step_achieved / HBM_PEAK_GBPS,
+                              "algorithmic_bytes_per_launch": step_bytes,
+                              "traffic": traffic_for("decode_step")}
+        result["indexer_roofline"] = {"kernel": "indexer_score_decode", "bound": "hbm", "achieved": achieved,
+                                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                                      "algorithmic_bytes_per_launch": idx_bytes,
+                                      "traffic": traffic_for("indexer_decode")}
+        log(f"one-launch step kernel {t_step_kernel * 1e3:.1f} us ({step_achieved:.0f} GB/s algorithmic)")
+    else:
+        result["roofline"] = {"kernel": "indexer_score_decode", "bound": "hbm", "achieved": achieved,
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                              "algorithmic_bytes_per_launch": idx_bytes,
+                              "traffic": traffic_for("indexer_decode")}
 
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {16 * args.cpu_layers} query-layers")

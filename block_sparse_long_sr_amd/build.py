@@ -27,7 +27,7 @@ DEVICE_FLAGS = [
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC"]
 
-SOURCES = ["api.cpp", "indexer_decode.hip", "topk_decode.hip", "attn.hip", "indexer_prefill.hip", "dense_attn.hip", "rope.hip", "attn_prefill.hip", "pool.cpp"]
+SOURCES = ["api.cpp", "indexer_decode.hip", "topk_decode.hip", "attn.hip", "indexer_prefill.hip", "dense_attn.hip", "rope.hip", "attn_prefill.hip", "decode_step.hip", "pool.cpp"]
 # Extra hipcc flags per source file (none at present).
 PER_FILE_FLAGS = {}
 

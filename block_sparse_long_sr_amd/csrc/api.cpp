@@ -301,6 +301,66 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
   return hip_status(uocr::launch_select_attn(sa, static_cast<hipStream_t>(stream)), "topk_attn_decode");
 }
 
+int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n_layers, const uint16_t* q_idx,
+                            const uint16_t* q, float* block_scores, int32_t* block_idx, int32_t* n_sel, float* out,
+                            float* lse, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_cfg(cfg));
+  TRY(check_kv(kv, true, true));
+  if (n_layers < 0) return fail(UOCR_ESHAPE, "n_layers must be >= 0 (got %d)", n_layers);
+  if (cfg->topk_blocks > uocr::kMaxFusedTopk)
+    return fail(UOCR_EUNSUPPORTED, "the one-launch decode step supports topk_blocks <= %d (got %d)",
+                uocr::kMaxFusedTopk, cfg->topk_blocks);
+  if ((int64_t)kv->max_blocks - cfg->local_blocks > uocr::kMaxFusedCandidates)
+    return fail(UOCR_EUNSUPPORTED, "the one-launch decode step supports max_blocks - local_blocks <= %d",
+                uocr::kMaxFusedCandidates);
+  if (n_layers == 0 || kv->batch == 0) return ok();
+  const uocr::DecodeStepPlan plan = uocr::decode_step_plan(n_layers, kv->batch, cfg->num_heads, kv->max_blocks);
+  if (plan.items >= ((int64_t)1 << 31))
+    return fail(UOCR_EUNSUPPORTED, "%lld work items (n_layers * batch * (ceil(max_blocks/32) + heads)) exceed 2^31",
+                (long long)plan.items);
+  REQ_PTR4(kv->ctx_lens, "kv->ctx_lens");
+  REQ_PTR16(q_idx, "q_idx");
+  REQ_PTR16(q, "q");
+  REQ_PTR4(block_scores, "block_scores");
+  REQ_PTR4(block_idx, "block_idx");
+  OPT_PTR4(n_sel, "n_sel");
+  REQ_PTR4(out, "out");
+  OPT_PTR4(lse, "lse");
+  TRY(check_page_gate(kv));
+  if (ws == nullptr) return fail(UOCR_EWORKSPACE, "ws is NULL (%zu bytes needed)", plan.ws_bytes);
+  if (ws_bytes < plan.ws_bytes)
+    return fail(UOCR_EWORKSPACE, "ws holds %zu bytes, %zu needed", ws_bytes, plan.ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(UOCR_EINVAL, "ws is not 256-byte aligned");
+  uocr::DecodeStepArgs a{};
+  a.k_pool = kv->k_pool;
+  a.v_pool = kv->v_pool;
+  a.kidx_pool = kv->kidx_pool;
+  a.kv_layer_stride = kv->num_blocks * cfg->num_heads * 32 * cfg->head_dim;
+  a.kidx_layer_stride = kv->num_blocks * 32 * cfg->index_dim;
+  a.block_table = kv->block_table;
+  a.ctx_lens = kv->ctx_lens;
+  a.block_page = kv->block_page;
+  a.query_page = kv->block_page != nullptr ? kv->query_page : nullptr;
+  a.q_idx = q_idx;
+  a.q = q;
+  a.block_scores = block_scores;
+  a.block_idx = block_idx;
+  a.out = out;
+  a.lse = lse;
+  a.n_sel = n_sel;
+  a.counters = static_cast<uint32_t*>(ws);
+  a.num_blocks = kv->num_blocks;
+  a.n_layers = n_layers;
+  a.batch = kv->batch;
+  a.max_blocks = kv->max_blocks;
+  a.heads = cfg->num_heads;
+  a.topk = cfg->topk_blocks;
+  a.local_blocks = cfg->local_blocks;
+  a.lag = plan.lag;
+  a.scale_log2 = cfg->sm_scale * 1.44269504088896340736f;
+  return hip_status(uocr::launch_decode_step(a, plan, static_cast<hipStream_t>(stream)), "sparse_decode_step");
+}
+
 int uocr_dense_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q, float* out, float* lse,
                            void* ws, size_t ws_bytes, void* stream) {
   TRY(check_cfg(cfg));
@@ -481,6 +541,8 @@ size_t uocr_workspace_size(const uocr_sparse_cfg* cfg, int32_t op, int32_t rows,
   switch (op) {
     case UOCR_OP_DENSE_ATTN_DECODE:
       return uocr::dense_plan(rows, cfg->num_heads, max_blocks).ws_bytes;
+    case UOCR_OP_DECODE_STEP:
+      return uocr::decode_step_plan(1, rows, cfg->num_heads, max_blocks).ws_bytes;
     case UOCR_OP_ATTN_PREFILL:
       return uocr::prefill_attn_plan(rows, cfg->num_heads, cfg->topk_blocks, max_blocks).ws_bytes;
     case UOCR_OP_INDEXER_PREFILL:

@@ -19,20 +19,12 @@ namespace uocr {
 
 namespace {
 constexpr int kAttnThreads = 1024;
-constexpr int kAttnWaves = kAttnThreads / kWave;
 }  // namespace
 
 // Attention of query qi, head h over the kept blocks in sel[0 .. topk)
 // (global or LDS memory); every thread of the 1024-thread workgroup calls it.
 __device__ __forceinline__ void attend_query(const AttnArgs& a, int qi, int h, const int32_t* sel) {
-  __shared__ float s_m[kAttnWaves];
-  __shared__ float s_l[kAttnWaves];
-  __shared__ float s_o[kAttnWaves][kDim];
-
-  const int lane = lane_id();
-  const int wave = wave_id();
-  const int c8 = (lane & 15) * 8; // first dim of the lane's slice
-
+  __shared__ AttendSmem<kAttnThreads> sm;
   int seq, p;
   if (a.prefill) {
     seq = 0;
@@ -42,55 +34,9 @@ __device__ __forceinline__ void attend_query(const AttnArgs& a, int qi, int h, c
     p = clamp_ctx(a.ctx_lens[qi], a.max_blocks) - 1;
   }
   const int64_t head_row = (int64_t)qi * a.heads + h;
-  const uint4 qv = *reinterpret_cast<const uint4*>(a.q + head_row * kDim + c8);
-  const int32_t* table = a.block_table + (int64_t)seq * a.max_blocks;
-
-  float m = -INFINITY;  // running max (log2 units), wave-uniform
-  float l = 0.0f;       // running sum over this lane's key group
-  float o[8];
-#pragma unroll
-  for (int d = 0; d < 8; ++d) o[d] = 0.0f;
-
-  for (int e = wave; e < a.topk; e += kAttnWaves) {
-    const int j = __builtin_amdgcn_readfirstlane(sel[e]);
-    if (j < 0 || j >= a.max_blocks || j * kBlock > p) continue;
-    const int pb = __builtin_amdgcn_readfirstlane(table[j]);
-    if (pb < 0 || (int64_t)pb >= a.num_blocks) continue;
-    const int64_t tile = ((int64_t)pb * a.heads + h) * (kBlock * kDim);
-    attend_block(a.k_pool + tile, a.v_pool + tile, j, p, qv, a.scale_log2, m, l, o);
-  }
-
-  reduce_key_groups(l, o);
-  if (lane == 0) {
-    s_m[wave] = m;
-    s_l[wave] = l;
-  }
-  if (lane < 16) {
-#pragma unroll
-    for (int d = 0; d < 8; ++d) s_o[wave][c8 + d] = o[d];
-  }
-  __syncthreads();
-
-  if (threadIdx.x < kDim) {
-    const int d = threadIdx.x;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w]);
-    float res = 0.0f, lse_v = -INFINITY;
-    if (M != -INFINITY) {
-      float Lsum = 0.0f, acc = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
-        const float f = exp2f(s_m[w] - M);
-        Lsum += s_l[w] * f;
-        acc += s_o[w][d] * f;
-      }
-      res = acc / Lsum;
-      lse_v = (M + log2f(Lsum)) * kLn2;
-    }
-    a.out[head_row * kDim + d] = res;
-    if (a.lse != nullptr && d == 0) a.lse[head_row] = lse_v;
-  }
+  attend_query_wg<kAttnThreads>(a.k_pool, a.v_pool, a.block_table + (int64_t)seq * a.max_blocks, a.num_blocks,
+                                a.heads, h, a.max_blocks, p, a.q + head_row * kDim, sel, a.topk, a.scale_log2,
+                                a.out + head_row * kDim, a.lse != nullptr ? a.lse + head_row : nullptr, sm);
 }
 
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {

@@ -89,4 +89,80 @@ __device__ __forceinline__ void reduce_key_groups(float& l, float (&o)[8]) {
   }
 }
 
+// LDS of attend_query_wg: one online-softmax state per wave.
+template <int NT>
+struct AttendSmem {
+  float m[NT / kWave];
+  float l[NT / kWave];
+  float o[NT / kWave][kDim];
+};
+
+// Attention of one query head at position p over the kept blocks
+// sel[0 .. topk) (global or LDS memory; -1 and out-of-range entries, blocks
+// starting after p and blocks whose pool index is out of range are
+// skipped).  The blocks are split over the NT/64 waves of the workgroup
+// (split-K), whose states are merged through LDS; every thread calls it.
+//   k_pool, v_pool : [num_blocks][heads][32][128] bf16;  table : the
+//   sequence's block-table row;  q_head : the head's 128 query dims;
+//   out_head : 128 floats;  lse_out : one float or null (natural log).
+template <int NT>
+__device__ __forceinline__ void attend_query_wg(const uint16_t* k_pool, const uint16_t* v_pool, const int32_t* table,
+                                                int64_t num_blocks, int heads, int h, int max_blocks, int p,
+                                                const uint16_t* q_head, const int32_t* sel, int topk,
+                                                float scale_log2, float* out_head, float* lse_out,
+                                                AttendSmem<NT>& sm) {
+  constexpr int NW = NT / kWave;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int c8 = (lane & 15) * 8;  // first dim of the lane's slice
+  const uint4 qv = *reinterpret_cast<const uint4*>(q_head + c8);
+
+  float m = -INFINITY;  // running max (log2 units), wave-uniform
+  float l = 0.0f;       // running sum over this lane's key group
+  float o[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) o[d] = 0.0f;
+
+  for (int e = wave; e < topk; e += NW) {
+    const int j = __builtin_amdgcn_readfirstlane(sel[e]);
+    if (j < 0 || j >= max_blocks || j * kBlock > p) continue;
+    const int pb = __builtin_amdgcn_readfirstlane(table[j]);
+    if (pb < 0 || (int64_t)pb >= num_blocks) continue;
+    const int64_t tile = ((int64_t)pb * heads + h) * (kBlock * kDim);
+    attend_block(k_pool + tile, v_pool + tile, j, p, qv, scale_log2, m, l, o);
+  }
+
+  reduce_key_groups(l, o);
+  if (lane == 0) {
+    sm.m[wave] = m;
+    sm.l[wave] = l;
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) sm.o[wave][c8 + d] = o[d];
+  }
+  __syncthreads();
+
+  if (threadIdx.x < kDim) {
+    const int d = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w]);
+    float res = 0.0f, lse_v = -INFINITY;
+    if (M != -INFINITY) {
+      float Lsum = 0.0f, acc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = exp2f(sm.m[w] - M);
+        Lsum += sm.l[w] * f;
+        acc += sm.o[w][d] * f;
+      }
+      res = acc / Lsum;
+      lse_v = (M + log2f(Lsum)) * kLn2;
+    }
+    out_head[d] = res;
+    if (lse_out != nullptr && d == 0) *lse_out = lse_v;
+  }
+}
+
 }  // namespace uocr

@@ -3,15 +3,11 @@
 // remote-candidate block is scored against the one-head 128-dim indexer
 // query, and each block keeps the maximum of its 32 key scores.
 //
-// The indexer-K cache is streamed once at HBM rate.  One wave scores one
-// 8 KB block: load k (k = 0..7) brings, in lane order, 1 KB = 4 key rows, so
-// lane l holds dims 8*(l%16)..+8 of key 4k + l/16 and every load instruction
-// reads a fully contiguous 1 KB.  The lane's 8-dim slice of the query stays
-// in registers; partial dots (v_dot2_f32_bf16, fp32 accumulate of exact
-// bf16 products) are summed over the 16 lanes of a DPP row, the block max is
-// taken in-lane over k and across the four rows with two lane swaps
-// (v_permlane16_swap, v_permlane32_swap).
+// The indexer-K cache is streamed once at HBM rate: one wave scores one 8 KB
+// block at a time (score_block_wave in indexer_common.h), the workgroups of
+// a sequence split its blocks into chunks.
 #include "device_common.h"
+#include "indexer_common.h"
 #include "kernels.h"
 
 namespace uocr {
@@ -40,24 +36,9 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerDecodeArgs a
 
   for (int j = j0 + wave; j < jend; j += nwaves) {
     const int pb = __builtin_amdgcn_readfirstlane(table[j]);
-    float score;
-    if (pb < 0 || (int64_t)pb >= a.num_blocks) {
-      score = __builtin_nanf("");
-    } else {
-      const uint4* base = reinterpret_cast<const uint4*>(a.kidx_pool + (int64_t)pb * (kBlock * kDim));
-      uint4 kv[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) kv[k] = base[k * kWave + lane];
-      float m = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) m = max_keep_nan(m, row16_sum(dot8_bf16(kv[k], qv)));
-      float a, b;
-      swap16(m, a, b);
-      m = max_keep_nan(a, b);
-      swap32(m, a, b);
-      m = max_keep_nan(a, b);
-      score = m;
-    }
+    const float score = (pb < 0 || (int64_t)pb >= a.num_blocks)
+                            ? __builtin_nanf("")
+                            : score_block_wave(a.kidx_pool + (int64_t)pb * (kBlock * kDim), qv);
     if (lane == 0) out[j] = score;
   }
 }

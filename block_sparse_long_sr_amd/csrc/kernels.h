@@ -87,6 +87,49 @@ struct SelAttnArgs {
 };
 hipError_t launch_select_attn(const SelAttnArgs& a, hipStream_t stream);
 
+// The whole decode step of a batch over n_layers layers in one launch
+// (scoring, selection and attention as ticket-ordered work items).  Pools,
+// queries and outputs are layer-major: layer l of k_pool/v_pool starts at
+// l * kv_layer_stride elements, of kidx_pool at l * kidx_layer_stride;
+// q_idx [L][B][Di], q [L][B][H][D], block_scores [L][B][M], block_idx
+// [L][B][topk], out [L][B][H][D], lse [L][B][H], n_sel [L][B].
+struct DecodeStepArgs {
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const uint16_t* kidx_pool;
+  int64_t kv_layer_stride;
+  int64_t kidx_layer_stride;
+  const int32_t* block_table;  // [B][M], shared by the layers
+  const int32_t* ctx_lens;     // [B]
+  const int32_t* block_page;   // [B][M] page tags or null
+  const int32_t* query_page;   // [B]
+  const uint16_t* q_idx;
+  const uint16_t* q;
+  float* block_scores;
+  int32_t* block_idx;
+  float* out;
+  float* lse;                  // or null
+  int32_t* n_sel;              // or null
+  uint32_t* counters;          // workspace: ticket, error word, per-slot completion counts
+  int64_t num_blocks;
+  int32_t n_layers;
+  int32_t batch;
+  int32_t max_blocks;
+  int32_t heads;
+  int32_t topk;
+  int32_t local_blocks;
+  int32_t lag;
+  float scale_log2;
+};
+struct DecodeStepPlan {
+  int32_t lag;            // slots between a slot's scoring and its attention items
+  int64_t counter_words;  // 2 + 2 * n_layers * batch
+  int64_t items;          // work items of the launch
+  size_t ws_bytes;
+};
+DecodeStepPlan decode_step_plan(int32_t n_layers, int32_t batch, int32_t heads, int32_t max_blocks);
+hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& plan, hipStream_t stream);
+
 // Dense full-context decode attention (comparator): split-K partials in a
 // workspace, then a merge.
 struct DensePlan {

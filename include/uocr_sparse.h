@@ -66,7 +66,8 @@ enum {
   UOCR_OP_INDEXER_PREFILL = 3,
   UOCR_OP_TOPK_PREFILL = 4,
   UOCR_OP_ATTN_PREFILL = 5,
-  UOCR_OP_DENSE_ATTN_DECODE = 6
+  UOCR_OP_DENSE_ATTN_DECODE = 6,
+  UOCR_OP_DECODE_STEP = 7      /* rows = n_layers * batch */
 };
 
 /*
@@ -201,6 +202,45 @@ int uocr_sparse_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const
 int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q,
                           const float* block_scores, int32_t* block_idx, int32_t* n_sel, float* out, float* lse,
                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The decode step of a batch over n_layers layers in ONE launch: for every
+ * layer l and sequence b, steps 2, 3 and 4 of uocr_indexer_score_decode,
+ * uocr_block_topk_decode and uocr_sparse_attn_decode (news.rkmt.cn/news/25027
+ * Sec. 5 steps 2-4), with the same scores and selections bit for bit and the
+ * same attention up to float32 summation order.  Work items (32-block
+ * scoring chunks and per-head selection + attention) are taken in a fixed
+ * ticket order by a grid that stays resident; a sequence's attention starts
+ * as soon as its own scoring is done, and layer l + 1 of a sequence starts
+ * after its layer l attention, so scoring of some sequences overlaps the
+ * selection and attention of others with no launch gaps.
+ * kv describes layer 0 and holds every layer, layer-major:
+ *   kv->k_pool, kv->v_pool : [n_layers][num_blocks][H][32][D] bf16
+ *   kv->kidx_pool          : [n_layers][num_blocks][32][Di] bf16
+ *   block_table, ctx_lens and the page tags are shared by the layers.
+ *   q_idx        : [n_layers][batch][Di] bf16
+ *   q            : [n_layers][batch][H][D] bf16
+ *   block_scores : [n_layers][batch][max_blocks] float32, written
+ *   block_idx    : [n_layers][batch][topk_blocks] int32, written
+ *   n_sel        : [n_layers][batch] int32 or NULL
+ *   out          : [n_layers][batch][H][D] float32, written
+ *   lse          : [n_layers][batch][H] float32 or NULL
+ *   ws           : workspace of uocr_workspace_size(cfg, UOCR_OP_DECODE_STEP,
+ *                  n_layers * batch, max_blocks) bytes, 256-byte aligned
+ *                  (completion counters; a clear kernel zeroes them at the
+ *                  start of the call, so stale contents do not matter).  The
+ *                  second 32-bit word is nonzero after the call if a
+ *                  dependency wait gave up after about a second (never
+ *                  expected; the results are then undefined).  Calls that
+ *                  share a workspace must be stream-ordered.
+ * Requires topk_blocks <= 256, max_blocks - local_blocks <= 16384 and
+ * n_layers * batch * (ceil(max_blocks / 32) + H) < 2^31 work items;
+ * UOCR_EUNSUPPORTED otherwise.  UOCR_EWORKSPACE when ws is NULL or too
+ * small, UOCR_EINVAL when it is not 256-byte aligned.
+ */
+int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n_layers, const uint16_t* q_idx,
+                            const uint16_t* q, float* block_scores, int32_t* block_idx, int32_t* n_sel, float* out,
+                            float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Dense full-context decode attention, the comparator for the pages'

@@ -158,6 +158,33 @@ def test_fused_decode_argument_checks(U):
     assert U.workspace_size(cfg, 2, 16, 4096) == 0
 
 
+def test_decode_step_argument_checks(U):
+    cfg = U.make_cfg()
+    need = U.workspace_size(cfg, U.OP_DECODE_STEP, 12 * 2, 8)
+    assert need == -(-((2 + 3 * 24) * 4) // 256) * 256  # ticket, error word, three counters per slot
+    ws = (0x100000, need)  # 256-byte aligned fake address; never dereferenced
+
+    def call(kv=None, n_layers=12, ws=ws, c=cfg, q_idx=FAKE):
+        U.sparse_decode_step(c, kv or _kv(U), n_layers, q_idx, FAKE, FAKE, FAKE, FAKE, ws=ws, stream=0)
+
+    for kwargs, code, text in (
+            (dict(ws=None), 3, "ws"), (dict(ws=(0x100000, need - 1)), 3, "ws"),
+            (dict(ws=(0x100000 + 16, need)), 1, "256"), (dict(n_layers=-1), 2, "n_layers"),
+            (dict(q_idx=None), 1, "q_idx"), (dict(kv=_kv(U, kidx_pool=None)), 1, "kidx_pool")):
+        with pytest.raises(U.UocrError) as e:
+            call(**kwargs)
+        assert e.value.status == code and text in U.last_error(), (kwargs, U.last_error())
+    big = U.make_cfg(topk_blocks=300, local_blocks=4)
+    with pytest.raises(U.UocrError) as e:
+        call(c=big)
+    assert e.value.status == 5
+    with pytest.raises(U.UocrError) as e:
+        call(kv=_kv(U, max_blocks=20000))
+    assert e.value.status == 5
+    call(n_layers=0)                    # nothing to do: no launch, no error
+    call(kv=_kv(U, batch=0), ws=None)
+
+
 def test_dense_decode_argument_checks(U):
     cfg = U.make_cfg()
     need = U.workspace_size(cfg, U.OP_DENSE_ATTN_DECODE, 16, 4096)

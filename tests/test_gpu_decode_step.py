@@ -1,0 +1,184 @@
+"""GPU parity of the one-launch decode step (uocr_sparse_decode_step: every
+layer's scoring, selection and attention as ticket-ordered work items)
+through the C ABI: block scores and selections bit for bit equal to the
+separate entry points, attention against the oracle (news.rkmt.cn/news/25027
+Sec. 5 steps 2-4) and within float32 summation-order noise of the separate
+attention kernel."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import block_sparse_long_sr_amd as U  # noqa: E402
+import oracle  # noqa: E402
+from synth import device as SD  # noqa: E402
+from synth import workloads as W  # noqa: E402
+import gpu_harness as G  # noqa: E402
+
+
+def _wl(name, seed, lens, layers, values="normal"):
+    lens = np.asarray(lens, np.int64)
+    return W.Workload(name=name, seed=seed, batch=len(lens), layers=layers, ctx_lens=lens,
+                      max_blocks=int(max(1, -(-int(lens.max()) // 32))), values=values)
+
+
+def _i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def run_step(dev, cfg, tags=None, qpages=None, fill=0xA7):
+    """One call over every resident layer; returns host copies and the
+    workspace's error word."""
+    wl = dev.wl
+    nl, B, M, H, D = dev.q.shape[0], wl.batch, wl.max_blocks, wl.heads, wl.head_dim
+    topk = cfg.topk_blocks
+    bp = _i32(tags) if tags is not None else None
+    qp = _i32(qpages) if qpages is not None else None
+    kv = U.make_kv(dev.k[0], dev.v[0], dev.kidx[0], dev.block_table, dev.ctx_lens, wl.pool_blocks, B, M, bp, qp)
+    scores = torch.full((nl, B, M), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((nl, B, topk), -7, dtype=torch.int32, device="cuda")
+    nsel = torch.full((nl, B), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((nl, B, H, D), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((nl, B, H), float("nan"), dtype=torch.float32, device="cuda")
+    wsb = U.workspace_size(cfg, U.OP_DECODE_STEP, nl * B, M)
+    assert wsb > 0
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    ws.fill_(fill)  # stale counters must not matter: the call clears them
+    U.sparse_decode_step(cfg, kv, nl, dev.q_idx, dev.q, scores, idx, out, lse, n_sel=nsel, ws=ws)
+    torch.cuda.synchronize()
+    err = int(ws[4:8].cpu().numpy().view(np.uint32)[0])
+    return {"scores": scores.cpu().numpy(), "idx": idx.cpu().numpy(), "nsel": nsel.cpu().numpy(),
+            "out": out.cpu().numpy(), "lse": lse.cpu().numpy(), "err": err}
+
+
+def separate(dev, cfg, li, tags=None, qpages=None):
+    """Layer li through the separate scoring launch and the fused
+    selection + attention launch."""
+    wl = dev.wl
+    B, M, H, D = wl.batch, wl.max_blocks, wl.heads, wl.head_dim
+    bp = _i32(tags) if tags is not None else None
+    qp = _i32(qpages) if qpages is not None else None
+    kv = U.make_kv(dev.k[li], dev.v[li], dev.kidx[li], dev.block_table, dev.ctx_lens, wl.pool_blocks, B, M, bp, qp)
+    scores = torch.full((B, M), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((B, cfg.topk_blocks), -7, dtype=torch.int32, device="cuda")
+    nsel = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((B, H, D), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
+    U.indexer_score_decode(cfg, kv, dev.q_idx[li], scores)
+    U.topk_attn_decode(cfg, kv, dev.q[li], scores, idx, out, lse, n_sel=nsel)
+    torch.cuda.synchronize()
+    return {"scores": scores.cpu().numpy(), "idx": idx.cpu().numpy(), "nsel": nsel.cpu().numpy(),
+            "out": out.cpu().numpy(), "lse": lse.cpu().numpy()}
+
+
+def compare_with_separate(dev, cfg, res, tags=None, qpages=None):
+    for li in range(dev.q.shape[0]):
+        ref = separate(dev, cfg, li, tags, qpages)
+        np.testing.assert_array_equal(res["scores"][li].view(np.uint32), ref["scores"].view(np.uint32),
+                                      err_msg=f"layer {li} block scores")
+        np.testing.assert_array_equal(res["idx"][li], ref["idx"], err_msg=f"layer {li} selection")
+        np.testing.assert_array_equal(res["nsel"][li], ref["nsel"])
+        fin = np.isfinite(ref["lse"])
+        assert np.array_equal(fin, np.isfinite(res["lse"][li]))
+        assert np.all(np.isneginf(res["lse"][li][~fin]))
+        np.testing.assert_allclose(res["lse"][li][fin], ref["lse"][fin], rtol=0, atol=1e-5)
+        np.testing.assert_allclose(res["out"][li], ref["out"], rtol=0, atol=1e-5)
+
+
+def oracle_check(wl, res, layer, b, cfg_o, tags=None, qpage=None):
+    L = int(wl.ctx_lens[b])
+    kidx = wl.kidx(layer, b, 0, L)
+    if tags is None:
+        ref = oracle.decode_query_fetch(wl.q(layer, b), wl.q_idx(layer, b), kidx, G.fetcher(wl, layer, b), L, cfg_o)
+    else:
+        ref = oracle.decode_query_fetch(wl.q(layer, b), wl.q_idx(layer, b), kidx, G.fetcher(wl, layer, b), L, cfg_o,
+                                        tags[b], int(qpage))
+    G.check_scores(res["scores"][layer, b], ref, wl.q_idx(layer, b), kidx, wl.max_blocks)
+    G.check_selection(res["idx"][layer, b], ref, cfg_o.topk_blocks)
+    got = [int(x) for x in res["idx"][layer, b] if x >= 0]
+    if got == ref["selected"]:
+        G.check_attention(res["out"][layer, b], res["lse"][layer, b], ref["out"], ref["lse"])
+    else:
+        o2, l2 = G.oracle_attend_with(wl, layer, b, wl.q(layer, b), got, L - 1, cfg_o)
+        G.check_attention(res["out"][layer, b], res["lse"][layer, b], o2, l2)
+
+
+def test_ragged_batch_three_layers():
+    lens = [0, 1, 31, 33, 127, 129, 513, 4097, 9999, 20001]
+    wl = _wl("step ragged", 0x5701, lens, layers=3)
+    print("case: decode step ragged", lens, "3 layers", flush=True)
+    dev = SD.generate(wl)
+    cfg = G.cfg_for(wl)
+    res = run_step(dev, cfg)
+    assert res["err"] == 0
+    compare_with_separate(dev, cfg, res)
+    for layer, b in ((0, 9), (2, 7), (1, 2), (2, 0)):
+        oracle_check(wl, res, layer, b, G.ocfg())
+
+
+def test_batch_of_one_is_layer_serial_and_repeatable():
+    # batch 1: no overlap across sequences; layer l + 1 waits for layer l
+    wl = _wl("step one sequence", 0x5702, [12345], layers=4)
+    print("case: decode step B=1, 4 layers, twice", flush=True)
+    dev = SD.generate(wl)
+    cfg = G.cfg_for(wl)
+    r1 = run_step(dev, cfg, fill=0x00)
+    r2 = run_step(dev, cfg, fill=0xFF)
+    assert r1["err"] == 0 and r2["err"] == 0
+    for k in ("scores", "out", "lse"):
+        np.testing.assert_array_equal(r1[k].view(np.uint32), r2[k].view(np.uint32), err_msg=k)
+    np.testing.assert_array_equal(r1["idx"], r2["idx"])
+    compare_with_separate(dev, cfg, r1)
+    oracle_check(wl, r1, 3, 0, G.ocfg())
+
+
+@pytest.mark.parametrize("topk,local", [(16, 4), (8, 1), (64, 2)])
+def test_topk_variants(topk, local):
+    lens = [3000, 65, 7777, 600, 2049]
+    wl = _wl(f"step topk {topk}", 0x5703 + topk, lens, layers=2, values="small_int")
+    print("case: decode step topk", topk, "local", local, flush=True)
+    dev = SD.generate(wl)
+    cfg = G.cfg_for(wl, topk, local)
+    res = run_step(dev, cfg)
+    assert res["err"] == 0
+    compare_with_separate(dev, cfg, res)
+    oracle_check(wl, res, 1, 2, G.ocfg(topk, local))
+
+
+def test_page_tags():
+    g = np.random.default_rng(0x5704)
+    lens = [8000, 3000, 12000, 500, 5000, 9000]
+    wl = _wl("step page tags", 0x5704, lens, layers=2)
+    print("case: decode step with page tags", flush=True)
+    dev = SD.generate(wl)
+    M = wl.max_blocks
+    tags = (np.arange(M)[None, :] // g.integers(20, 60, (wl.batch, 1))).astype(np.int32)
+    qpages = np.array([g.integers(0, max(1, int(tags[b, max(0, -(-lens[b] // 32) - 1)]) + 1))
+                       for b in range(wl.batch)], np.int32)
+    cfg = G.cfg_for(wl)
+    res = run_step(dev, cfg, tags, qpages)
+    assert res["err"] == 0
+    compare_with_separate(dev, cfg, res, tags, qpages)
+    oracle_check(wl, res, 1, 2, G.ocfg(), tags, qpages[2])
+
+
+def test_full_headline_workload_sampled():
+    """16 sequences x 12 layers at 131072 tokens, the measured configuration:
+    every layer bitwise against the separate launches, sampled queries
+    against the oracle."""
+    torch.cuda.empty_cache()
+    wl = W.config3()
+    print("case: decode step", wl.name, flush=True)
+    dev = SD.generate(wl)
+    cfg = G.cfg_for(wl)
+    res = run_step(dev, cfg)
+    assert res["err"] == 0
+    compare_with_separate(dev, cfg, res)
+    for layer, b in ((0, 0), (11, 15)):
+        oracle_check(wl, res, layer, b, G.ocfg())
+    del dev
+    torch.cuda.empty_cache()
