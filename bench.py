@@ -255,15 +255,28 @@ def run_page_gate(U, SD, W, torch, reps=20):
         U.indexer_score_decode(cfg, kv, dev.q_idx[0], scores, stream=sh)
         U.topk_attn_decode(cfg, kv, dev.q[0], scores, idx, out, lse, stream=sh)
 
+    ws1 = torch.empty(U.workspace_size(cfg, U.OP_DECODE_STEP, B, M), dtype=torch.uint8, device="cuda")
+    scores1 = scores.view(1, B, M)
+
+    def one_launch(kv):
+        U.sparse_decode_step(cfg, kv, 1, dev.q_idx, dev.q, scores1, idx.view(1, B, 16), out.view(1, B, H, 128),
+                             lse.view(1, B, H), ws=ws1, stream=sh, schedule=U.STEP_ONE_LAUNCH)
+
     t_plain = timed(lambda: step(kv_plain))
     t_gate = timed(lambda: step(kv_gate))
+    t1_plain = timed(lambda: one_launch(kv_plain))
+    t1_gate = timed(lambda: one_launch(kv_gate))
     idx_b, topk_b, attn_b = decode_bytes(wl)
     step_bytes = idx_b + topk_b + attn_b
     res["decode"] = {"workload": wl.name, "queries": B, "algorithmic_bytes": step_bytes,
-                     "us": {"plain": t_plain * 1e3, "page_aware": t_gate * 1e3},
-                     "query_heads_per_s": {"plain": B * H / (t_plain * 1e-3), "page_aware": B * H / (t_gate * 1e-3)},
-                     "hbm_GBps_page_aware": step_bytes / (t_gate * 1e-3) / 1e9}
-    del dev, scores, out
+                     "us": {"plain": t_plain * 1e3, "page_aware": t_gate * 1e3,
+                            "one_launch_plain": t1_plain * 1e3, "one_launch_page_aware": t1_gate * 1e3},
+                     "query_heads_per_s": {"plain": B * H / (t_plain * 1e-3), "page_aware": B * H / (t_gate * 1e-3),
+                                           "one_launch_plain": B * H / (t1_plain * 1e-3),
+                                           "one_launch_page_aware": B * H / (t1_gate * 1e-3)},
+                     "hbm_GBps_page_aware": step_bytes / (t_gate * 1e-3) / 1e9,
+                     "hbm_GBps_one_launch_page_aware": step_bytes / (t1_gate * 1e-3) / 1e9}
+    del dev, scores, out, ws1
     torch.cuda.empty_cache()
 
     wl = W.config5()
@@ -468,7 +481,8 @@ def main():
 
     def step():
         if one_launch:
-            U.sparse_decode_step(cfg, kv0, L, dev.q_idx, dev.q, scores, idx, out, lse, ws=step_ws, stream=sh)
+            U.sparse_decode_step(cfg, kv0, L, dev.q_idx, dev.q, scores, idx, out, lse, ws=step_ws, stream=sh,
+                                 schedule=U.STEP_ONE_LAUNCH)
             return
         for l in range(L):
             for b0, b1, gkv, st in groups:
@@ -675,7 +689,8 @@ def main():
         log("page-aware ranking: ragged multi-page decode and the 128K prefill chunk, with and without page tags")
         result["page_gate"] = run_page_gate(U, SD, W, torch)
         pg = result["page_gate"]
-        log(f"page-aware decode {pg['decode']['us']['page_aware']:.1f} us (plain {pg['decode']['us']['plain']:.1f} us); "
+        log(f"page-aware decode {pg['decode']['us']['page_aware']:.1f} us (plain {pg['decode']['us']['plain']:.1f} us), "
+            f"one launch {pg['decode']['us']['one_launch_page_aware']:.1f} us (plain {pg['decode']['us']['one_launch_plain']:.1f} us); "
             f"prefill scoring+merge {pg['prefill_scoring_and_merge']['us']['page_aware']:.1f} us "
             f"(plain {pg['prefill_scoring_and_merge']['us']['plain']:.1f} us)")
 

@@ -22,7 +22,7 @@ __all__ = [
     "workspace_size", "status_string", "last_error", "abi_version",
     "OP_INDEXER_DECODE", "OP_TOPK_DECODE", "OP_ATTN_DECODE",
     "OP_INDEXER_PREFILL", "OP_TOPK_PREFILL", "OP_ATTN_PREFILL", "OP_DENSE_ATTN_DECODE", "dense_attn_decode",
-    "OP_DECODE_STEP", "sparse_decode_step",
+    "OP_DECODE_STEP", "sparse_decode_step", "STEP_AUTO", "STEP_ONE_LAUNCH", "STEP_PER_LAYER",
     "rope_cache_write", "rope_queries", "page_coords", "BlockPool", "PageWindow",
 ]
 
@@ -33,6 +33,7 @@ OP_INDEXER_DECODE, OP_TOPK_DECODE, OP_ATTN_DECODE = 0, 1, 2
 OP_INDEXER_PREFILL, OP_TOPK_PREFILL, OP_ATTN_PREFILL = 3, 4, 5
 OP_DENSE_ATTN_DECODE = 6
 OP_DECODE_STEP = 7
+STEP_AUTO, STEP_ONE_LAUNCH, STEP_PER_LAYER = 0, 1, 2
 
 
 class SparseCfg(ctypes.Structure):
@@ -94,7 +95,7 @@ _SIGS = {
     "uocr_sparse_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "uocr_topk_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "uocr_dense_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
-    "uocr_sparse_decode_step": ([_CFG, _KV, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "uocr_sparse_decode_step": ([_CFG, _KV, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "uocr_rope_cache_write": ([_CFG, _KV, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "uocr_rope_queries": ([_CFG, ctypes.c_int32, _P, _P, _P, _P, _P], ctypes.c_int),
     "uocr_indexer_score_prefill": ([_CFG, _KV, _P, _I32, _I32, _P, _SZ, _P], ctypes.c_int),
@@ -205,10 +206,12 @@ def dense_attn_decode(cfg: SparseCfg, kv: KV, q, out, lse=None, ws=None, stream=
 
 
 def sparse_decode_step(cfg: SparseCfg, kv: KV, n_layers: int, q_idx, q, block_scores, block_idx, out, lse=None,
-                       n_sel=None, ws=None, stream=None) -> None:
-    """Scoring, selection and attention of every layer of a batch in one
-    launch; ``kv`` describes layer 0 of layer-major pools."""
-    _check(_lib.uocr_sparse_decode_step(ctypes.byref(cfg), ctypes.byref(kv), int(n_layers), _ptr(q_idx), _ptr(q),
+                       n_sel=None, ws=None, stream=None, schedule: int = 0) -> None:
+    """Scoring, selection and attention of every layer of a batch;
+    ``kv`` describes layer 0 of layer-major pools.  ``schedule``:
+    STEP_AUTO, STEP_ONE_LAUNCH or STEP_PER_LAYER."""
+    _check(_lib.uocr_sparse_decode_step(ctypes.byref(cfg), ctypes.byref(kv), int(n_layers), int(schedule),
+                                        _ptr(q_idx), _ptr(q),
                                         _ptr(block_scores), _ptr(block_idx), _ptr(n_sel), _ptr(out), _ptr(lse),
                                         _ptr(ws), _nbytes(ws), _stream(stream)), "sparse_decode_step")
 

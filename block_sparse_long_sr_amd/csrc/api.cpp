@@ -301,12 +301,16 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
   return hip_status(uocr::launch_select_attn(sa, static_cast<hipStream_t>(stream)), "topk_attn_decode");
 }
 
-int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n_layers, const uint16_t* q_idx,
+int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n_layers, int32_t schedule,
+                            const uint16_t* q_idx,
                             const uint16_t* q, float* block_scores, int32_t* block_idx, int32_t* n_sel, float* out,
                             float* lse, void* ws, size_t ws_bytes, void* stream) {
   TRY(check_cfg(cfg));
   TRY(check_kv(kv, true, true));
   if (n_layers < 0) return fail(UOCR_ESHAPE, "n_layers must be >= 0 (got %d)", n_layers);
+  if (schedule != UOCR_STEP_AUTO && schedule != UOCR_STEP_ONE_LAUNCH && schedule != UOCR_STEP_PER_LAYER)
+    return fail(UOCR_EINVAL, "schedule must be UOCR_STEP_AUTO, UOCR_STEP_ONE_LAUNCH or UOCR_STEP_PER_LAYER (got %d)",
+                schedule);
   if (cfg->topk_blocks > uocr::kMaxFusedTopk)
     return fail(UOCR_EUNSUPPORTED, "the one-launch decode step supports topk_blocks <= %d (got %d)",
                 uocr::kMaxFusedTopk, cfg->topk_blocks);
@@ -316,7 +320,7 @@ int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32
   if (n_layers == 0 || kv->batch == 0) return ok();
   const uocr::DecodeStepPlan plan = uocr::decode_step_plan(n_layers, kv->batch, cfg->num_heads, kv->max_blocks);
   if (plan.items >= ((int64_t)1 << 31))
-    return fail(UOCR_EUNSUPPORTED, "%lld work items (n_layers * batch * (ceil(max_blocks/32) + heads)) exceed 2^31",
+    return fail(UOCR_EUNSUPPORTED, "%lld work items (n_layers * batch * (ceil(max_blocks/chunk) + heads)) exceed 2^31",
                 (long long)plan.items);
   REQ_PTR4(kv->ctx_lens, "kv->ctx_lens");
   REQ_PTR16(q_idx, "q_idx");
@@ -357,8 +361,13 @@ int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32
   a.topk = cfg->topk_blocks;
   a.local_blocks = cfg->local_blocks;
   a.lag = plan.lag;
+  a.chunk = plan.chunk;
   a.scale_log2 = cfg->sm_scale * 1.44269504088896340736f;
-  return hip_status(uocr::launch_decode_step(a, plan, static_cast<hipStream_t>(stream)), "sparse_decode_step");
+  const bool one_launch = schedule == UOCR_STEP_ONE_LAUNCH ||
+                          (schedule == UOCR_STEP_AUTO &&
+                           uocr::decode_step_one_launch(n_layers, kv->batch, kv->max_blocks));
+  return hip_status(uocr::launch_decode_step(a, plan, one_launch, static_cast<hipStream_t>(stream)),
+                    "sparse_decode_step");
 }
 
 int uocr_dense_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q, float* out, float* lse,

@@ -5,7 +5,7 @@
 //
 // Work items, handed out in ticket order by one atomic counter (a workgroup
 // takes its next ticket while it works on the current item):
-//   * scoring item (layer l, sequence b, chunk c): kStepChunk blocks of the
+//   * scoring item (layer l, sequence b, chunk c): `chunk` blocks of the
 //     sequence's candidates, two 8 KB blocks per wave in flight.  The
 //     workgroup that completes the last chunk of (l, b) then runs the
 //     selection of (l, b) once and publishes the kept block ids;
@@ -45,14 +45,6 @@ namespace {
 // workgroups share a CU and one's item boundary is covered by the other.
 constexpr int kStepThreads = 512;
 constexpr int kStepWaves = kStepThreads / kWave;
-#ifndef UOCR_STEP_CHUNK
-#define UOCR_STEP_CHUNK 32
-#endif
-// Blocks per scoring item: 32 blocks (256 KB of indexer keys) keep a slot's
-// scoring short (its items run side by side), and the ticket counter
-// sustains the resulting rate.
-constexpr int kStepChunk = UOCR_STEP_CHUNK;
-static_assert(kStepChunk % (2 * kStepWaves) == 0, "scoring items hold whole pairs of wave blocks");
 constexpr uint32_t kSpinLimit = 1u << 20;  // polls of one wait: a device-scope load (~1 us) + s_sleep 2 each, about a second
 
 struct Item {
@@ -126,7 +118,8 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
   const int wave = wave_id();
   const int B = a.batch, M = a.max_blocks, H = a.heads;
   const int S = a.n_layers * B;
-  const int C = (M + kStepChunk - 1) / kStepChunk;
+  const int chunk = a.chunk;  // a multiple of 2 * kStepWaves
+  const int C = (M + chunk - 1) / chunk;
   const int D = a.lag;  // < B, so every wait is on a lower ticket
   const uint32_t total = (uint32_t)S * (uint32_t)(C + H);
   uint32_t* ticket = a.counters;
@@ -156,8 +149,8 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
         if (tid == 0) wait_count(attn_done + (it.slot - B), (uint32_t)H, err);
         __syncthreads();
       }
-      const int j0 = it.idx * kStepChunk;
-      const int jend_all = min(j0 + kStepChunk, M);
+      const int j0 = it.idx * chunk;
+      const int jend_all = min(j0 + chunk, M);
       for (int j = max(j0, ncand) + tid; j < jend_all; j += kStepThreads) publish(scores + j, -INFINITY);
       const int jend = min(jend_all, ncand);
       if (j0 < jend) {
@@ -232,9 +225,13 @@ DecodeStepPlan decode_step_plan(int32_t n_layers, int32_t batch, int32_t heads, 
   // is batch slots later.  Half the batch (below batch, as the ticket order
   // requires); measured best at 16 sequences x 128K.
   p.lag = batch / 2;
+  // Blocks per scoring item: 32 (256 KB of indexer keys) at long contexts,
+  // 16 below 2048 blocks, so that a sequence's scoring spreads over many
+  // workgroups and finishes soon after its first item starts.
+  p.chunk = max_blocks >= 2048 ? 32 : 16;
   p.counter_words = 2 + 3 * S;
   p.ws_bytes = (size_t)((p.counter_words * 4 + 255) / 256 * 256);
-  p.items = S * (((int64_t)max_blocks + kStepChunk - 1) / kStepChunk + heads);
+  p.items = S * (((int64_t)max_blocks + p.chunk - 1) / p.chunk + heads);
   return p;
 }
 
@@ -262,8 +259,67 @@ hipError_t launch_step(const DecodeStepArgs& a, int64_t items, hipStream_t strea
 }
 }  // namespace
 
-hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& plan, hipStream_t stream) {
+bool decode_step_one_launch(int32_t n_layers, int32_t batch, int32_t max_blocks) {
+  // The one launch overlaps one sequence's selection and attention with the
+  // scoring of others, but a sequence's layers stay in order: each layer of
+  // a sequence must be scored, selected and attended within the time the
+  // other sequences' scoring of that layer takes, about batch * max_blocks *
+  // 8 KB at HBM rate.  Measured at 16 sequences x 12 layers: per-layer
+  // launches win up to 64K tokens (2048 blocks), the one launch from 96K
+  // (3072 blocks); with one layer there is no layer order to overlap.
+  return n_layers >= 2 && (int64_t)batch * max_blocks >= 40960;
+}
+
+hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& plan, bool one_launch,
+                              hipStream_t stream) {
   if (a.batch == 0 || a.n_layers == 0) return hipSuccess;
+  const int B = a.batch, M = a.max_blocks, H = a.heads;
+  if (!one_launch) {
+    // per-layer launches of the scoring kernel and the fused selection +
+    // attention kernel, on the caller's stream
+    for (int l = 0; l < a.n_layers; ++l) {
+      IndexerDecodeArgs ia{};
+      ia.kidx_pool = a.kidx_pool + (int64_t)l * a.kidx_layer_stride;
+      ia.block_table = a.block_table;
+      ia.ctx_lens = a.ctx_lens;
+      ia.q_idx = a.q_idx + (int64_t)l * B * kDim;
+      ia.block_scores = a.block_scores + (int64_t)l * B * M;
+      ia.num_blocks = a.num_blocks;
+      ia.batch = B;
+      ia.max_blocks = M;
+      ia.local_blocks = a.local_blocks;
+      ia.chunk = indexer_decode_chunk(B, M);
+      hipError_t e = launch_indexer_decode(ia, stream);
+      if (e != hipSuccess) return e;
+      SelAttnArgs sa{};
+      AttnArgs& at = sa.attn;
+      at.k_pool = a.k_pool + (int64_t)l * a.kv_layer_stride;
+      at.v_pool = a.v_pool + (int64_t)l * a.kv_layer_stride;
+      at.block_table = a.block_table;
+      at.ctx_lens = a.ctx_lens;
+      at.q = a.q + (int64_t)l * B * H * kDim;
+      at.block_idx = nullptr;
+      at.out = a.out + (int64_t)l * B * H * kDim;
+      at.lse = a.lse != nullptr ? a.lse + (int64_t)l * B * H : nullptr;
+      at.num_blocks = a.num_blocks;
+      at.nq = B;
+      at.heads = H;
+      at.max_blocks = M;
+      at.topk = a.topk;
+      at.scale_log2 = a.scale_log2;
+      at.prefill = 0;
+      at.q_start = 0;
+      sa.block_scores = ia.block_scores;
+      sa.block_idx_out = a.block_idx + (int64_t)l * B * a.topk;
+      sa.n_sel = a.n_sel != nullptr ? a.n_sel + (int64_t)l * B : nullptr;
+      sa.local_blocks = a.local_blocks;
+      sa.block_page = a.block_page;
+      sa.query_page = a.query_page;
+      e = launch_select_attn(sa, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   hipLaunchKernelGGL(decode_step_clear_kernel, dim3(1), dim3(kStepThreads), 0, stream, a.counters,
                      (int)plan.counter_words);
   hipError_t e = hipGetLastError();

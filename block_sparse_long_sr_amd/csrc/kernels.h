@@ -119,16 +119,22 @@ struct DecodeStepArgs {
   int32_t topk;
   int32_t local_blocks;
   int32_t lag;
+  int32_t chunk;               // blocks per scoring item, a multiple of 16
   float scale_log2;
 };
 struct DecodeStepPlan {
   int32_t lag;            // slots between a slot's scoring and its attention items
+  int32_t chunk;          // blocks per scoring item
   int64_t counter_words;  // 2 + 2 * n_layers * batch
   int64_t items;          // work items of the launch
   size_t ws_bytes;
 };
 DecodeStepPlan decode_step_plan(int32_t n_layers, int32_t batch, int32_t heads, int32_t max_blocks);
-hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& plan, hipStream_t stream);
+// Whether the automatic schedule runs the step as one launch (otherwise as
+// per-layer launches of the scoring and fused selection + attention kernels).
+bool decode_step_one_launch(int32_t n_layers, int32_t batch, int32_t max_blocks);
+hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& plan, bool one_launch,
+                              hipStream_t stream);
 
 // Dense full-context decode attention (comparator): split-K partials in a
 // workspace, then a merge.

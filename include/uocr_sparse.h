@@ -204,16 +204,22 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
- * The decode step of a batch over n_layers layers in ONE launch: for every
- * layer l and sequence b, steps 2, 3 and 4 of uocr_indexer_score_decode,
+ * The decode step of a batch over n_layers layers: for every layer l and
+ * sequence b, steps 2, 3 and 4 of uocr_indexer_score_decode,
  * uocr_block_topk_decode and uocr_sparse_attn_decode (news.rkmt.cn/news/25027
  * Sec. 5 steps 2-4), with the same scores and selections bit for bit and the
- * same attention up to float32 summation order.  Work items (32-block
- * scoring chunks and per-head selection + attention) are taken in a fixed
- * ticket order by a grid that stays resident; a sequence's attention starts
- * as soon as its own scoring is done, and layer l + 1 of a sequence starts
- * after its layer l attention, so scoring of some sequences overlaps the
- * selection and attention of others with no launch gaps.
+ * same attention up to float32 summation order; layer l + 1 of a sequence is
+ * computed after its layer l.  schedule:
+ *   UOCR_STEP_ONE_LAUNCH: ONE launch of the whole step.  Work items (scoring
+ *     chunks of 16 or 32 blocks, a sequence's selection, per-head attention)
+ *     are taken in a fixed ticket order by a grid that stays resident; a
+ *     sequence's selection and attention start as soon as its own scoring is
+ *     done, overlapping the scoring of other sequences, with no launch gaps.
+ *   UOCR_STEP_PER_LAYER: per layer, the scoring launch and the fused
+ *     selection + attention launch of uocr_topk_attn_decode.
+ *   UOCR_STEP_AUTO: the one launch when n_layers >= 2 and batch * max_blocks
+ *     >= 40960 (the one launch needs enough other sequences' scoring to hide
+ *     each sequence's layer-to-layer latency), otherwise per layer.
  * kv describes layer 0 and holds every layer, layer-major:
  *   kv->k_pool, kv->v_pool : [n_layers][num_blocks][H][32][D] bf16
  *   kv->kidx_pool          : [n_layers][num_blocks][32][Di] bf16
@@ -226,19 +232,24 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
  *   out          : [n_layers][batch][H][D] float32, written
  *   lse          : [n_layers][batch][H] float32 or NULL
  *   ws           : workspace of uocr_workspace_size(cfg, UOCR_OP_DECODE_STEP,
- *                  n_layers * batch, max_blocks) bytes, 256-byte aligned
- *                  (completion counters; a clear kernel zeroes them at the
- *                  start of the call, so stale contents do not matter).  The
- *                  second 32-bit word is nonzero after the call if a
+ *                  n_layers * batch, max_blocks) bytes, 256-byte aligned,
+ *                  required whatever the schedule (completion counters of
+ *                  the one launch; a clear kernel zeroes them at the start
+ *                  of the call, so stale contents do not matter).  After a
+ *                  one-launch call the second 32-bit word is nonzero if a
  *                  dependency wait gave up after about a second (never
  *                  expected; the results are then undefined).  Calls that
  *                  share a workspace must be stream-ordered.
  * Requires topk_blocks <= 256, max_blocks - local_blocks <= 16384 and
- * n_layers * batch * (ceil(max_blocks / 32) + H) < 2^31 work items;
+ * n_layers * batch * (ceil(max_blocks / chunk) + H) < 2^31 work items
+ * (chunk = 32 blocks per scoring item from max_blocks 2048 up, 16 below);
  * UOCR_EUNSUPPORTED otherwise.  UOCR_EWORKSPACE when ws is NULL or too
- * small, UOCR_EINVAL when it is not 256-byte aligned.
+ * small, UOCR_EINVAL when it is not 256-byte aligned or schedule is not one
+ * of the three values.
  */
-int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n_layers, const uint16_t* q_idx,
+enum { UOCR_STEP_AUTO = 0, UOCR_STEP_ONE_LAUNCH = 1, UOCR_STEP_PER_LAYER = 2 };
+int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n_layers, int32_t schedule,
+                            const uint16_t* q_idx,
                             const uint16_t* q, float* block_scores, int32_t* block_idx, int32_t* n_sel, float* out,
                             float* lse, void* ws, size_t ws_bytes, void* stream);
 

@@ -164,13 +164,15 @@ def test_decode_step_argument_checks(U):
     assert need == -(-((2 + 3 * 24) * 4) // 256) * 256  # ticket, error word, three counters per slot
     ws = (0x100000, need)  # 256-byte aligned fake address; never dereferenced
 
-    def call(kv=None, n_layers=12, ws=ws, c=cfg, q_idx=FAKE):
-        U.sparse_decode_step(c, kv or _kv(U), n_layers, q_idx, FAKE, FAKE, FAKE, FAKE, ws=ws, stream=0)
+    def call(kv=None, n_layers=12, ws=ws, c=cfg, q_idx=FAKE, schedule=0):
+        U.sparse_decode_step(c, kv or _kv(U), n_layers, q_idx, FAKE, FAKE, FAKE, FAKE, ws=ws, stream=0,
+                             schedule=schedule)
 
     for kwargs, code, text in (
             (dict(ws=None), 3, "ws"), (dict(ws=(0x100000, need - 1)), 3, "ws"),
             (dict(ws=(0x100000 + 16, need)), 1, "256"), (dict(n_layers=-1), 2, "n_layers"),
-            (dict(q_idx=None), 1, "q_idx"), (dict(kv=_kv(U, kidx_pool=None)), 1, "kidx_pool")):
+            (dict(q_idx=None), 1, "q_idx"), (dict(kv=_kv(U, kidx_pool=None)), 1, "kidx_pool"),
+            (dict(schedule=3), 1, "schedule"), (dict(schedule=-1), 1, "schedule")):
         with pytest.raises(U.UocrError) as e:
             call(**kwargs)
         assert e.value.status == code and text in U.last_error(), (kwargs, U.last_error())
