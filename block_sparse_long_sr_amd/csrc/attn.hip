@@ -34,9 +34,16 @@ __device__ __forceinline__ void attend_query(const AttnArgs& a, int qi, int h, c
     p = clamp_ctx(a.ctx_lens[qi], a.max_blocks) - 1;
   }
   const int64_t head_row = (int64_t)qi * a.heads + h;
-  attend_query_wg<kAttnThreads>(a.k_pool, a.v_pool, a.block_table + (int64_t)seq * a.max_blocks, a.num_blocks,
-                                a.heads, h, a.max_blocks, p, a.q + head_row * kDim, sel, a.topk, a.scale_log2,
-                                a.out + head_row * kDim, a.lse != nullptr ? a.lse + head_row : nullptr, sm);
+  const int32_t* table = a.block_table + (int64_t)seq * a.max_blocks;
+  float* lse = a.lse != nullptr ? a.lse + head_row : nullptr;
+  if (a.prefill)  // rows of a chunk share tiles: cached loads
+    attend_query_wg<kAttnThreads, false>(a.k_pool, a.v_pool, table, a.num_blocks, a.heads, h, a.max_blocks, p,
+                                         a.q + head_row * kDim, sel, a.topk, a.scale_log2, a.out + head_row * kDim,
+                                         lse, sm);
+  else  // decode: every kept tile is read once
+    attend_query_wg<kAttnThreads, true>(a.k_pool, a.v_pool, table, a.num_blocks, a.heads, h, a.max_blocks, p,
+                                        a.q + head_row * kDim, sel, a.topk, a.scale_log2, a.out + head_row * kDim,
+                                        lse, sm);
 }
 
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {

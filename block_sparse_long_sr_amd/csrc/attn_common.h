@@ -18,15 +18,18 @@ namespace uocr {
 
 // The wave's share of a block's K and V tiles: lane l holds dims
 // 8*(l%16)..+8 of keys 4k + l/16, k = 0..7 (eight 1 KB loads per tile).
+// kStream: the tiles are read once by this launch (decode), so the loads
+// are non-temporal; prefill rows share tiles and keep ordinary loads.
+template <bool kStream>
 __device__ __forceinline__ void load_block_tiles(const uint16_t* k_tile, const uint16_t* v_tile, uint4 (&kv)[8],
                                                  uint4 (&vv)[8]) {
   const int lane = lane_id();
   const uint4* kt = reinterpret_cast<const uint4*>(k_tile);
   const uint4* vt = reinterpret_cast<const uint4*>(v_tile);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) kv[k] = kt[k * kWave + lane];
+  for (int k = 0; k < 8; ++k) kv[k] = kStream ? load_stream16(kt + k * kWave + lane) : kt[k * kWave + lane];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) vv[k] = vt[k * kWave + lane];
+  for (int k = 0; k < 8; ++k) vv[k] = kStream ? load_stream16(vt + k * kWave + lane) : vt[k * kWave + lane];
 }
 
 // Online-softmax update of (m, l, o) with block j of a query at position p,
@@ -71,10 +74,11 @@ __device__ __forceinline__ void attend_loaded_block(const uint4 (&kv)[8], const 
   m = m_new;
 }
 
+template <bool kStream>
 __device__ __forceinline__ void attend_block(const uint16_t* k_tile, const uint16_t* v_tile, int j, int p,
                                              const uint4& qv, float scale_log2, float& m, float& l, float (&o)[8]) {
   uint4 kv[8], vv[8];
-  load_block_tiles(k_tile, v_tile, kv, vv);
+  load_block_tiles<kStream>(k_tile, v_tile, kv, vv);
   attend_loaded_block(kv, vv, j, p, qv, scale_log2, m, l, o);
 }
 
@@ -102,10 +106,11 @@ struct AttendSmem {
 // starting after p and blocks whose pool index is out of range are
 // skipped).  The blocks are split over the NT/64 waves of the workgroup
 // (split-K), whose states are merged through LDS; every thread calls it.
+// kStream as for load_block_tiles.
 //   k_pool, v_pool : [num_blocks][heads][32][128] bf16;  table : the
 //   sequence's block-table row;  q_head : the head's 128 query dims;
 //   out_head : 128 floats;  lse_out : one float or null (natural log).
-template <int NT>
+template <int NT, bool kStream>
 __device__ __forceinline__ void attend_query_wg(const uint16_t* k_pool, const uint16_t* v_pool, const int32_t* table,
                                                 int64_t num_blocks, int heads, int h, int max_blocks, int p,
                                                 const uint16_t* q_head, const int32_t* sel, int topk,
@@ -129,7 +134,7 @@ __device__ __forceinline__ void attend_query_wg(const uint16_t* k_pool, const ui
     const int pb = __builtin_amdgcn_readfirstlane(table[j]);
     if (pb < 0 || (int64_t)pb >= num_blocks) continue;
     const int64_t tile = ((int64_t)pb * heads + h) * (kBlock * kDim);
-    attend_block(k_pool + tile, v_pool + tile, j, p, qv, scale_log2, m, l, o);
+    attend_block<kStream>(k_pool + tile, v_pool + tile, j, p, qv, scale_log2, m, l, o);
   }
 
   reduce_key_groups(l, o);

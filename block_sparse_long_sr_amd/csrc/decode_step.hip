@@ -45,6 +45,7 @@ namespace {
 // workgroups share a CU and one's item boundary is covered by the other.
 constexpr int kStepThreads = 512;
 constexpr int kStepWaves = kStepThreads / kWave;
+constexpr int kMaxStepChunk = 32;  // blocks per scoring item, at most
 constexpr uint32_t kSpinLimit = 1u << 20;  // polls of one wait: a device-scope load (~1 us) + s_sleep 2 each, about a second
 
 struct Item {
@@ -112,6 +113,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
   __shared__ int32_t s_blocks[kMaxFusedTopk];
   __shared__ uint32_t s_ticket;
   __shared__ int s_last;
+  __shared__ float s_chunk[kMaxStepChunk];  // an item's block scores
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -151,7 +153,6 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
       }
       const int j0 = it.idx * chunk;
       const int jend_all = min(j0 + chunk, M);
-      for (int j = max(j0, ncand) + tid; j < jend_all; j += kStepThreads) publish(scores + j, -INFINITY);
       const int jend = min(jend_all, ncand);
       if (j0 < jend) {
         const uint4 qv = *reinterpret_cast<const uint4*>(a.q_idx + (int64_t)it.slot * kDim + (lane & 15) * 8);
@@ -169,11 +170,15 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
           const float s1 = ok ? block_max_of_tile(kv, qv) : __builtin_nanf("");
           const float s2 = ok2 ? block_max_of_tile(kv2, qv) : __builtin_nanf("");
           if (lane == 0) {
-            publish(scores + j, s1);
-            if (j2 < jend) publish(scores + j2, s2);
+            s_chunk[j - j0] = s1;
+            if (j2 < jend) s_chunk[j2 - j0] = s2;
           }
         }
       }
+      __syncthreads();
+      // one coalesced store of the item's scores (non-candidates: -inf)
+      for (int j = j0 + tid; j < jend_all; j += kStepThreads)
+        publish(scores + j, j < jend ? s_chunk[j - j0] : -INFINITY);
       drain_stores();
       __syncthreads();
       if (tid == 0) {
@@ -204,9 +209,10 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
       const int h = it.idx;
       const int64_t head_row = (int64_t)it.slot * H + h;
       const int64_t kv_off = (int64_t)l * a.kv_layer_stride;
-      attend_query_wg<kStepThreads>(a.k_pool + kv_off, a.v_pool + kv_off, table, a.num_blocks, H, h, M, L - 1,
-                                    a.q + head_row * kDim, s_blocks, a.topk, a.scale_log2, a.out + head_row * kDim,
-                                    a.lse != nullptr ? a.lse + head_row : nullptr, att_sm);
+      attend_query_wg<kStepThreads, true>(a.k_pool + kv_off, a.v_pool + kv_off, table, a.num_blocks, H, h, M,
+                                          L - 1, a.q + head_row * kDim, s_blocks, a.topk, a.scale_log2,
+                                          a.out + head_row * kDim, a.lse != nullptr ? a.lse + head_row : nullptr,
+                                          att_sm);
       drain_stores();
       __syncthreads();
       if (tid == 0) count_done(attn_done + it.slot);
@@ -228,7 +234,7 @@ DecodeStepPlan decode_step_plan(int32_t n_layers, int32_t batch, int32_t heads, 
   // Blocks per scoring item: 32 (256 KB of indexer keys) at long contexts,
   // 16 below 2048 blocks, so that a sequence's scoring spreads over many
   // workgroups and finishes soon after its first item starts.
-  p.chunk = max_blocks >= 2048 ? 32 : 16;
+  p.chunk = max_blocks >= 2048 ? kMaxStepChunk : 16;
   p.counter_words = 2 + 3 * S;
   p.ws_bytes = (size_t)((p.counter_words * 4 + 255) / 256 * 256);
   p.items = S * (((int64_t)max_blocks + p.chunk - 1) / p.chunk + heads);
@@ -265,9 +271,10 @@ bool decode_step_one_launch(int32_t n_layers, int32_t batch, int32_t max_blocks)
   // a sequence must be scored, selected and attended within the time the
   // other sequences' scoring of that layer takes, about batch * max_blocks *
   // 8 KB at HBM rate.  Measured at 16 sequences x 12 layers: per-layer
-  // launches win up to 64K tokens (2048 blocks), the one launch from 96K
-  // (3072 blocks); with one layer there is no layer order to overlap.
-  return n_layers >= 2 && (int64_t)batch * max_blocks >= 40960;
+  // launches win up to 64K tokens (2048 blocks), the two are even at 96K
+  // (3072 blocks) and the one launch wins at 128K; with one layer there is
+  // no layer order to overlap.
+  return n_layers >= 2 && (int64_t)batch * max_blocks >= 57344;
 }
 
 hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& plan, bool one_launch,

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn_partial_kernel(Dense
     const int pb = __builtin_amdgcn_readfirstlane(table[j]);
     if (pb < 0 || (int64_t)pb >= a.num_blocks) continue;
     const int64_t tile = ((int64_t)pb * a.heads + h) * (kBlock * kDim);
-    attend_block(a.k_pool + tile, a.v_pool + tile, j, p, qv, a.scale_log2, m, l, o);
+    attend_block<true>(a.k_pool + tile, a.v_pool + tile, j, p, qv, a.scale_log2, m, l, o);
   }
   reduce_key_groups(l, o);
   if (lane == 0) {

@@ -17,12 +17,12 @@
 namespace uocr {
 
 // The wave's share of one 8 KB tile: lane l gets dims 8*(l%16)..+8 of keys
-// 4k + l/16, k = 0..7.
+// 4k + l/16, k = 0..7 (non-temporal loads: every tile is read once).
 __device__ __forceinline__ void load_index_tile(const uint16_t* tile, uint4 (&kv)[8]) {
   const uint4* base = reinterpret_cast<const uint4*>(tile);
   const int lane = lane_id();
 #pragma unroll
-  for (int k = 0; k < 8; ++k) kv[k] = base[k * kWave + lane];
+  for (int k = 0; k < 8; ++k) kv[k] = load_stream16(base + k * kWave + lane);
 }
 
 // Block max of a tile already in registers (every lane gets it).

@@ -218,7 +218,7 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
  *   UOCR_STEP_PER_LAYER: per layer, the scoring launch and the fused
  *     selection + attention launch of uocr_topk_attn_decode.
  *   UOCR_STEP_AUTO: the one launch when n_layers >= 2 and batch * max_blocks
- *     >= 40960 (the one launch needs enough other sequences' scoring to hide
+ *     >= 57344 (the one launch needs enough other sequences' scoring to hide
  *     each sequence's layer-to-layer latency), otherwise per layer.
  * kv describes layer 0 and holds every layer, layer-major:
  *   kv->k_pool, kv->v_pool : [n_layers][num_blocks][H][32][D] bf16
