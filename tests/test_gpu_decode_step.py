@@ -224,3 +224,65 @@ def test_context_above_4096_candidate_blocks():
     assert res["err"] == 0
     compare_with_separate(dev, cfg, res)
     oracle_check(wl, res, 1, 0, G.ocfg())
+
+
+def test_out_of_range_pool_blocks():
+    """Block-table entries outside the pool (-1, >= num_blocks): their blocks
+    score NaN, rank last and are never attended, exactly as in the separate
+    launches."""
+    lens = [9000, 3000, 12345, 700]
+    wl = _wl("step bad table", 0x5706, lens, layers=2)
+    print("case: decode step with out-of-range table entries", flush=True)
+    dev = SD.generate(wl)
+    tab = dev.block_table.cpu().numpy().copy()
+    g = np.random.default_rng(0x5706)
+    for b, L in enumerate(lens):
+        nb = -(-L // 32)
+        for j in g.choice(nb, size=min(nb, 7), replace=False):
+            tab[b, j] = -1 if g.random() < 0.5 else wl.pool_blocks + int(g.integers(0, 1000))
+    dev.block_table.copy_(torch.from_numpy(tab))
+    cfg = G.cfg_for(wl)
+    res = run_step(dev, cfg)
+    assert res["err"] == 0
+    compare_with_separate(dev, cfg, res)
+    assert np.isnan(res["scores"]).any()
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two one-launch calls with their own workspaces running at the same
+    time on two streams give the results of the calls run one after the
+    other."""
+    wl = _wl("step concurrent", 0x5707, [20000, 7000, 15000, 30000, 1000, 25000], layers=3)
+    print("case: decode step, two concurrent calls", flush=True)
+    dev = SD.generate(wl)
+    cfg = G.cfg_for(wl)
+    ref = run_step(dev, cfg)
+    nl, B, M, H, D = dev.q.shape[0], wl.batch, wl.max_blocks, wl.heads, wl.head_dim
+    halves = [(0, 3), (3, 6)]
+    outs = []
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    keep = []
+    torch.cuda.synchronize()
+    for (b0, b1), st in zip(halves, streams):
+        nb = b1 - b0
+        kv = U.make_kv(dev.k[0], dev.v[0], dev.kidx[0], dev.block_table[b0:b1], dev.ctx_lens[b0:b1],
+                       wl.pool_blocks, nb, M)
+        qi = dev.q_idx[:, b0:b1].contiguous()
+        q = dev.q[:, b0:b1].contiguous()
+        sc = torch.full((nl, nb, M), float("nan"), dtype=torch.float32, device="cuda")
+        ix = torch.full((nl, nb, 16), -7, dtype=torch.int32, device="cuda")
+        o = torch.full((nl, nb, H, D), float("nan"), dtype=torch.float32, device="cuda")
+        ls = torch.full((nl, nb, H), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.full((U.workspace_size(cfg, U.OP_DECODE_STEP, nl * nb, M),), 0x33, dtype=torch.uint8,
+                        device="cuda")
+        torch.cuda.synchronize()
+        keep.append((kv, qi, q, ws))
+        U.sparse_decode_step(cfg, kv, nl, qi, q, sc, ix, o, ls, ws=ws, stream=st, schedule=U.STEP_ONE_LAUNCH)
+        outs.append((b0, b1, sc, ix, o, ls, ws))
+    torch.cuda.synchronize()
+    for b0, b1, sc, ix, o, ls, ws in outs:
+        assert int(ws[4:8].cpu().numpy().view(np.uint32)[0]) == 0
+        np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), ref["scores"][:, b0:b1].view(np.uint32))
+        np.testing.assert_array_equal(ix.cpu().numpy(), ref["idx"][:, b0:b1])
+        np.testing.assert_array_equal(o.cpu().numpy().view(np.uint32), ref["out"][:, b0:b1].view(np.uint32))
+        np.testing.assert_array_equal(ls.cpu().numpy().view(np.uint32), ref["lse"][:, b0:b1].view(np.uint32))
