@@ -414,7 +414,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the decode step shards by sequence with no communication, see DESIGN.md)", file=sys.stderr)
+              "(the decode step shards by sequence with no communication across GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
