@@ -30,7 +30,7 @@ def _i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
-def run_step(dev, cfg, tags=None, qpages=None, fill=0xA7, schedule=U.STEP_ONE_LAUNCH):
+def run_step(dev, cfg, tags=None, qpages=None, fill=0xA7, schedule=U.STEP_ONE_LAUNCH, optional=True):
     """One call over every resident layer (by default forced to the one
     launch, whatever the automatic choice); returns host copies and the
     workspace's error word."""
@@ -49,7 +49,8 @@ def run_step(dev, cfg, tags=None, qpages=None, fill=0xA7, schedule=U.STEP_ONE_LA
     assert wsb > 0
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     ws.fill_(fill)  # stale counters must not matter: the call clears them
-    U.sparse_decode_step(cfg, kv, nl, dev.q_idx, dev.q, scores, idx, out, lse, n_sel=nsel, ws=ws, schedule=schedule)
+    U.sparse_decode_step(cfg, kv, nl, dev.q_idx, dev.q, scores, idx, out, lse if optional else None,
+                         n_sel=nsel if optional else None, ws=ws, schedule=schedule)
     torch.cuda.synchronize()
     err = int(ws[4:8].cpu().numpy().view(np.uint32)[0])
     return {"scores": scores.cpu().numpy(), "idx": idx.cpu().numpy(), "nsel": nsel.cpu().numpy(),
@@ -124,6 +125,11 @@ def test_ragged_batch_three_layers():
     for sched in (U.STEP_PER_LAYER, U.STEP_AUTO):
         r2 = run_step(dev, cfg, schedule=sched)
         compare_with_separate(dev, cfg, r2, atol=0)
+    # lse and n_sel are optional outputs: left NULL, nothing else changes
+    r3 = run_step(dev, cfg, optional=False)
+    for k in ("scores", "idx", "out"):
+        np.testing.assert_array_equal(r3[k].view(np.uint32), res[k].view(np.uint32), err_msg=k)
+    assert np.all(np.isnan(r3["lse"])) and np.all(r3["nsel"] == -7)
 
 
 def test_batch_of_one_is_layer_serial_and_repeatable():
@@ -170,6 +176,8 @@ def test_page_tags():
     assert res["err"] == 0
     compare_with_separate(dev, cfg, res, tags, qpages)
     oracle_check(wl, res, 1, 2, G.ocfg(), tags, qpages[2])
+    r2 = run_step(dev, cfg, tags, qpages, schedule=U.STEP_PER_LAYER)
+    compare_with_separate(dev, cfg, r2, tags, qpages, atol=0)
 
 
 def test_full_headline_workload_sampled():
