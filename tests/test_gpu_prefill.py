@@ -81,6 +81,16 @@ def test_prefill_64_splits_sampled():
     check_prefill(wl, rows)
 
 
+def test_prefill_full_chunk_sampled():
+    """The measured chunk: T=2048 rows at q_start=129024 of a 131072-token
+    context (64 splits of 64 blocks), in the bench's launch configuration
+    (block-major attention), sampled rows against the oracle."""
+    wl = W.config5()
+    print("case:", wl.name, flush=True)
+    rows = [0, 1, 31, 32, 511, 512, 1024, 2047] + list(range(7, 2048, 331))
+    check_prefill(wl, sorted(set(rows)))
+
+
 def test_prefill_nan_key_in_candidate_block_ranks_last():
     """As the decode case: a NaN indexer key makes its block's score NaN in
     the MFMA scoring too, and that block ranks last for every row."""
