@@ -294,3 +294,41 @@ def test_concurrent_calls_on_two_streams():
         np.testing.assert_array_equal(ix.cpu().numpy(), ref["idx"][:, b0:b1])
         np.testing.assert_array_equal(o.cpu().numpy().view(np.uint32), ref["out"][:, b0:b1].view(np.uint32))
         np.testing.assert_array_equal(ls.cpu().numpy().view(np.uint32), ref["lse"][:, b0:b1].view(np.uint32))
+
+
+def test_graph_capture_and_replays():
+    """The one-launch step captured in a HIP graph (its counters are cleared
+    by a kernel, not a memset) and replayed several times with eager work in
+    between: every replay equals the eager call bit for bit."""
+    wl = _wl("step graph", 0x5708, [9000, 30000, 4097, 12345], layers=3)
+    print("case: decode step in a HIP graph", flush=True)
+    dev = SD.generate(wl)
+    cfg = G.cfg_for(wl)
+    ref = run_step(dev, cfg)
+    nl, B, M, H, D = dev.q.shape[0], wl.batch, wl.max_blocks, wl.heads, wl.head_dim
+    kv = U.make_kv(dev.k[0], dev.v[0], dev.kidx[0], dev.block_table, dev.ctx_lens, wl.pool_blocks, B, M)
+    scores = torch.zeros((nl, B, M), dtype=torch.float32, device="cuda")
+    idx = torch.zeros((nl, B, 16), dtype=torch.int32, device="cuda")
+    out = torch.zeros((nl, B, H, D), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((nl, B, H), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(U.workspace_size(cfg, U.OP_DECODE_STEP, nl * B, M), dtype=torch.uint8, device="cuda")
+    cap = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cap):
+        U.sparse_decode_step(cfg, kv, nl, dev.q_idx, dev.q, scores, idx, out, lse, ws=ws,
+                             stream=cap.cuda_stream, schedule=U.STEP_ONE_LAUNCH)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in (scores, out, lse):
+            x.fill_(float("nan"))
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(ws[4:8].cpu().numpy().view(np.uint32)[0]) == 0
+        np.testing.assert_array_equal(scores.cpu().numpy().view(np.uint32), ref["scores"].view(np.uint32))
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"])
+        np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref["out"].view(np.uint32))
+        np.testing.assert_array_equal(lse.cpu().numpy().view(np.uint32), ref["lse"].view(np.uint32))
+        run_step(dev, cfg)  # eager work between replays
