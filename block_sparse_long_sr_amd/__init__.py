@@ -267,12 +267,15 @@ class BlockPool:
             raise ValueError(f"uocr_pool_create: {last_error()}")
 
     def close(self) -> None:
-        if self._h:
-            _lib.uocr_pool_destroy(self._h)
-            self._h = None
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            _lib.uocr_pool_destroy(h)
 
     def __del__(self):
-        self.close()
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown: the library may already be gone
+            pass
 
     def append(self, seq: int, n_tokens: int) -> None:
         _check(_lib.uocr_pool_append(self._h, int(seq), int(n_tokens)), "pool_append")

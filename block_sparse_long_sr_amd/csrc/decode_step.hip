@@ -31,6 +31,8 @@
 // acquire fence (an L1/L2 invalidation of its XCD) before reading, so it
 // cannot hit a stale line.  No L2 write-back is needed on the writer's side.
 // A clear kernel zeroes the counters before each launch.
+#include <atomic>
+
 #include "attn_common.h"
 #include "device_common.h"
 #include "indexer_common.h"
@@ -246,20 +248,24 @@ template <int KPT>
 hipError_t launch_step(const DecodeStepArgs& a, int64_t items, hipStream_t stream) {
   // One resident wave of workgroups (they loop over the tickets); a grid
   // larger than what fits is also correct, the extra groups find no ticket.
-  static int resident[64] = {0};
+  // The count is computed once per device (threads that race here store
+  // the same value).
+  static std::atomic<int> resident[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (resident[dev] == 0) {
+  int fit = resident[dev].load(std::memory_order_relaxed);
+  if (fit == 0) {
     int per_cu = 0, cus = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_step_kernel<KPT>, kStepThreads, 0);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    resident[dev] = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+    fit = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+    resident[dev].store(fit, std::memory_order_relaxed);
   }
-  const int64_t grid = items < resident[dev] ? items : resident[dev];
+  const int64_t grid = items < fit ? items : fit;
   hipLaunchKernelGGL(decode_step_kernel<KPT>, dim3((unsigned)grid), dim3(kStepThreads), 0, stream, a);
   return hipGetLastError();
 }

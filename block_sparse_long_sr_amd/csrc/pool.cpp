@@ -51,6 +51,18 @@ int32_t take_id(uocr_pool* p) {
   return id;
 }
 
+// Host allocations can fail; no C++ exception crosses the C ABI.
+template <typename F>
+int guarded(F&& body) {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    return uocr::set_error(UOCR_EINVAL, "out of host memory");
+  } catch (...) {
+    return uocr::set_error(UOCR_EINVAL, "unexpected host error");
+  }
+}
+
 int check_seq(const uocr_pool* p, int32_t seq) {
   if (p == nullptr) return uocr::set_error(UOCR_EINVAL, "pool is NULL");
   if (seq < 0 || seq >= (int32_t)p->seq_blocks.size())
@@ -66,67 +78,78 @@ uocr_pool* uocr_pool_create(int32_t num_blocks, int32_t max_seqs) {
     uocr::set_error(UOCR_ESHAPE, "num_blocks and max_seqs must be >= 0 (got %d, %d)", num_blocks, max_seqs);
     return nullptr;
   }
-  uocr_pool* p = new (std::nothrow) uocr_pool;
-  if (p == nullptr) {
-    uocr::set_error(UOCR_EINVAL, "out of host memory");
+  uocr_pool* p = nullptr;
+  const int st = guarded([&] {
+    p = new uocr_pool;
+    p->num_blocks = num_blocks;
+    p->free_ids.resize(num_blocks);
+    for (int32_t i = 0; i < num_blocks; ++i) p->free_ids[i] = i;  // ascending order is already a min-heap
+    p->seq_blocks.resize(max_seqs);
+    p->seq_len.assign(max_seqs, 0);
+    return uocr::set_error(UOCR_OK, "");
+  });
+  if (st != UOCR_OK) {
+    delete p;
     return nullptr;
   }
-  p->num_blocks = num_blocks;
-  p->free_ids.resize(num_blocks);
-  for (int32_t i = 0; i < num_blocks; ++i) p->free_ids[i] = i;  // ascending order is already a min-heap
-  p->seq_blocks.resize(max_seqs);
-  p->seq_len.assign(max_seqs, 0);
-  uocr::set_error(UOCR_OK, "");
   return p;
 }
 
 void uocr_pool_destroy(uocr_pool* pool) { delete pool; }
 
 int uocr_pool_append(uocr_pool* pool, int32_t seq, int64_t n_tokens) {
-  if (int st = check_seq(pool, seq)) return st;
-  if (n_tokens < 0) return uocr::set_error(UOCR_ESHAPE, "n_tokens must be >= 0 (got %lld)", (long long)n_tokens);
-  const int64_t need = blocks_for(pool->seq_len[seq] + n_tokens) - (int64_t)pool->seq_blocks[seq].size();
-  if (need > (int64_t)pool->free_ids.size())
-    return uocr::set_error(UOCR_ECAPACITY, "pool exhausted: %lld more blocks needed, %zu free", (long long)need,
-                           pool->free_ids.size());
-  for (int64_t i = 0; i < need; ++i) pool->seq_blocks[seq].push_back(take_id(pool));
-  pool->seq_len[seq] += n_tokens;
-  pool->used += need;
-  pool->peak = std::max(pool->peak, pool->used);
-  return uocr::set_error(UOCR_OK, "");
+  return guarded([&] {
+    if (int st = check_seq(pool, seq)) return st;
+    if (n_tokens < 0) return uocr::set_error(UOCR_ESHAPE, "n_tokens must be >= 0 (got %lld)", (long long)n_tokens);
+    const int64_t need = blocks_for(pool->seq_len[seq] + n_tokens) - (int64_t)pool->seq_blocks[seq].size();
+    if (need > (int64_t)pool->free_ids.size())
+      return uocr::set_error(UOCR_ECAPACITY, "pool exhausted: %lld more blocks needed, %zu free", (long long)need,
+                             pool->free_ids.size());
+    if (need > 0) pool->seq_blocks[seq].reserve(pool->seq_blocks[seq].size() + need);  // may throw: nothing changed yet
+    for (int64_t i = 0; i < need; ++i) pool->seq_blocks[seq].push_back(take_id(pool));
+    pool->seq_len[seq] += n_tokens;
+    pool->used += need;
+    pool->peak = std::max(pool->peak, pool->used);
+    return uocr::set_error(UOCR_OK, "");
+  });
 }
 
 int uocr_pool_keep(uocr_pool* pool, int32_t seq, const int64_t* ranges, int32_t n_ranges) {
-  if (int st = check_seq(pool, seq)) return st;
-  if (n_ranges < 0 || (n_ranges > 0 && ranges == nullptr))
-    return uocr::set_error(UOCR_EINVAL, "ranges must hold n_ranges >= 0 pairs");
-  const int64_t len = pool->seq_len[seq];
-  std::vector<char> keep(pool->seq_blocks[seq].size(), 0);
-  int64_t prev_hi = 0;
-  for (int32_t r = 0; r < n_ranges; ++r) {
-    const int64_t lo = ranges[2 * r], hi = ranges[2 * r + 1];
-    if (lo < prev_hi || hi < lo || hi > len)
-      return uocr::set_error(UOCR_ESHAPE, "range %d [%lld, %lld) not ascending inside [0, %lld)", r, (long long)lo,
-                             (long long)hi, (long long)len);
-    prev_hi = hi;
-    if (hi == lo) continue;  // an empty range keeps nothing
-    for (int64_t b = lo / kBlockTokens; b < blocks_for(hi); ++b) keep[b] = 1;
-  }
-  std::vector<int32_t> kept, dropped;
-  int64_t last_fill = 0;
-  const int64_t nblk = (int64_t)pool->seq_blocks[seq].size();
-  for (int64_t b = 0; b < nblk; ++b) {
-    if (keep[b]) {
-      kept.push_back(pool->seq_blocks[seq][b]);
-      last_fill = (b == nblk - 1) ? len - b * kBlockTokens : kBlockTokens;
-    } else {
-      dropped.push_back(pool->seq_blocks[seq][b]);
+  return guarded([&] {
+    if (int st = check_seq(pool, seq)) return st;
+    if (n_ranges < 0 || (n_ranges > 0 && ranges == nullptr))
+      return uocr::set_error(UOCR_EINVAL, "ranges must hold n_ranges >= 0 pairs");
+    const int64_t len = pool->seq_len[seq];
+    std::vector<char> keep(pool->seq_blocks[seq].size(), 0);
+    int64_t prev_hi = 0;
+    for (int32_t r = 0; r < n_ranges; ++r) {
+      const int64_t lo = ranges[2 * r], hi = ranges[2 * r + 1];
+      if (lo < prev_hi || hi < lo || hi > len)
+        return uocr::set_error(UOCR_ESHAPE, "range %d [%lld, %lld) not ascending inside [0, %lld)", r, (long long)lo,
+                               (long long)hi, (long long)len);
+      prev_hi = hi;
+      if (hi == lo) continue;  // an empty range keeps nothing
+      for (int64_t b = lo / kBlockTokens; b < blocks_for(hi); ++b) keep[b] = 1;
     }
-  }
-  pool->seq_blocks[seq] = kept;
-  pool->seq_len[seq] = kept.empty() ? 0 : (int64_t)(kept.size() - 1) * kBlockTokens + last_fill;
-  release_ids(pool, dropped);
-  return uocr::set_error(UOCR_OK, "");
+    std::vector<int32_t> kept, dropped;
+    int64_t last_fill = 0;
+    const int64_t nblk = (int64_t)pool->seq_blocks[seq].size();
+    for (int64_t b = 0; b < nblk; ++b) {
+      if (keep[b]) {
+        kept.push_back(pool->seq_blocks[seq][b]);
+        last_fill = (b == nblk - 1) ? len - b * kBlockTokens : kBlockTokens;
+      } else {
+        dropped.push_back(pool->seq_blocks[seq][b]);
+      }
+    }
+    pool->free_ids.reserve(pool->free_ids.size() + dropped.size());  // may throw: nothing changed yet
+    pool->seq_blocks[seq].swap(kept);
+    pool->seq_len[seq] = pool->seq_blocks[seq].empty()
+                             ? 0
+                             : (int64_t)(pool->seq_blocks[seq].size() - 1) * kBlockTokens + last_fill;
+    release_ids(pool, dropped);
+    return uocr::set_error(UOCR_OK, "");
+  });
 }
 
 int uocr_pool_table(const uocr_pool* pool, int32_t seq, int32_t* table, int32_t max_blocks, int64_t* length) {
