@@ -407,6 +407,8 @@ def main():
     ap.add_argument("--no-page-gate", action="store_true", help="skip the page-aware ranking measurement")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense full-context comparator")
     ap.add_argument("--no-rope", action="store_true", help="skip the page2d cache-write measurement")
+    ap.add_argument("--no-layout", action="store_true",
+                    help="skip the decode step on the contiguous block layout")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the chunked-prefill case (profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -675,7 +677,39 @@ def main():
         log(f"dense full-context attention step {ms_dense:.2f} ms ({dense_bytes / (ms_dense * 1e-3) / 1e9:.0f} GB/s): "
             f"sparse step is {ms_dense / ms_step:.1f}x faster")
         del dws
-    del dev, scores, out
+    del dev, kvs, groups
+    torch.cuda.empty_cache()
+    if one_launch and not args.no_layout:
+        # The same step with every sequence's blocks in consecutive pool slots
+        # (what a fresh lowest-id-first block pool hands out), against the
+        # seeded random placement of the headline figure.
+        wl_c = W.config3()
+        wl_c.layout = "contiguous"
+        dev = SD.generate(wl_c)
+        kv_c = dev.kv(0)
+
+        def step_c():
+            U.sparse_decode_step(cfg, kv_c, L, dev.q_idx, dev.q, scores, idx, out, lse, ws=step_ws, stream=sh,
+                                 schedule=U.STEP_ONE_LAUNCH)
+
+        for _ in range(args.warmup):
+            step_c()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        for _ in range(args.steps):
+            step_c()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        ms_c = a_.elapsed_time(b_) / args.steps
+        result["contiguous_layout"] = {
+            "what": "the same step with each sequence's blocks in consecutive pool slots (headline: seeded random "
+                    "placement)",
+            "ms_per_step": ms_c, "query_heads_per_s": B * L * H / (ms_c * 1e-3),
+            "step_hbm_GBps": step_bytes / (ms_c * 1e-3) / 1e9}
+        log(f"contiguous block layout: decode step {ms_c * 1e3:.1f} us ({step_bytes / (ms_c * 1e-3) / 1e9:.0f} GB/s)")
+        del dev, kv_c
+        torch.cuda.empty_cache()
+    del scores, out
     torch.cuda.empty_cache()
     if not args.no_prefill:
         log("chunked prefill T=2048 at 129024 of 131072")

@@ -70,6 +70,7 @@ class Workload:
     rows: int = 0                   # prefill only (T)
     edits: List[Edit] = field(default_factory=list)
     notes: str = ""
+    layout: str = "permuted"        # "permuted": pool blocks in a seeded random order; "contiguous": in order
 
     # ---- derived structure -------------------------------------------------
     def nblocks(self, b: int) -> int:
@@ -85,7 +86,10 @@ class Workload:
     def block_table(self) -> np.ndarray:
         """int32 [B, max_blocks]; unused entries are -1."""
         P = self.pool_blocks
-        perm = rng.permutation(self.key(ROLE_STRUCT, 0xFFFF, 0), P)
+        if self.layout == "contiguous":
+            perm = np.arange(P, dtype=np.int64)  # each sequence a run of consecutive pool blocks
+        else:
+            perm = rng.permutation(self.key(ROLE_STRUCT, 0xFFFF, 0), P)
         tab = np.full((self.batch, self.max_blocks), -1, dtype=np.int32)
         off = 0
         for b in range(self.batch):
