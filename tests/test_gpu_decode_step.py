@@ -332,3 +332,19 @@ def test_graph_capture_and_replays():
         np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref["out"].view(np.uint32))
         np.testing.assert_array_equal(lse.cpu().numpy().view(np.uint32), ref["lse"].view(np.uint32))
         run_step(dev, cfg)  # eager work between replays
+
+
+def test_contiguous_block_layout():
+    """The workload generator's contiguous placement (each sequence's blocks
+    consecutive in the pool): same parity as the random placement."""
+    wl = _wl("step contiguous layout", 0x5709, [20000, 9000, 33000], layers=2)
+    wl.layout = "contiguous"
+    print("case: decode step, contiguous block layout", flush=True)
+    dev = SD.generate(wl)
+    tab = dev.block_table.cpu().numpy()
+    assert np.array_equal(tab[0, :10], np.arange(10))
+    cfg = G.cfg_for(wl)
+    res = run_step(dev, cfg)
+    assert res["err"] == 0
+    compare_with_separate(dev, cfg, res)
+    oracle_check(wl, res, 1, 2, G.ocfg())
