@@ -609,7 +609,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "layers": L, "ctx_len": int(wl.ctx_lens[0]),
                    "heads": H, "head_dim": 128, "block_size": 32, "topk_blocks": 16, "local_blocks": 4,
-                   "queries_per_step": B * L, "plant": wl.notes,
+                   "queries_per_step": B * L, "plant": wl.notes, "seed": hex(wl.seed),
                    "launches": "one uocr_sparse_decode_step per step" if one_launch else
                                f"per layer, {ns} micro-batch streams" + (", HIP graph" if args.graph else "")},
         "tokens_per_s": B / (ms_step * 1e-3),

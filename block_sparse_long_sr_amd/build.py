@@ -1,7 +1,8 @@
 """Build libuocr_sparse.so (gfx950) in-tree with hipcc.
 
 Usage: ``python block_sparse_long_sr_amd/build.py`` (a script: the package
-itself refuses to import until the library exists) or ``build()``.  Every call
+itself refuses to import until the library exists) or ``build()``;
+``build.py --host-sanitize DIR`` builds a host-side ASan/UBSan copy into DIR.  Every call
 recompiles every source; the objects go to ``_build/`` and the shared library
 next to this file, where the binding loads it.
 """
@@ -57,10 +58,30 @@ def compile_objects(sources, src_dir, obj_dir, extra=()):
     return [o for _, o in jobs], outs
 
 
-def link(objs, out_path):
+# Host-side AddressSanitizer + UBSan for the library's host code (argument
+# validation, planning, the block pool); device code is built as usual.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def link(objs, out_path, extra=()):
     tmp = out_path + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", tmp])
     os.replace(tmp, out_path)
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """Build a host-sanitized copy of the library and binding into
+    out_dir/block_sparse_long_sr_amd/ (run Python with LD_PRELOAD of the
+    clang ASan runtime and that directory first on sys.path)."""
+    import shutil
+    pkg = os.path.join(out_dir, "block_sparse_long_sr_amd")
+    os.makedirs(pkg, exist_ok=True)
+    shutil.copy(os.path.join(PKG, "__init__.py"), pkg)
+    objs, _ = compile_objects(SOURCES, CSRC, os.path.join(ROOT, "_build", "uocr_sparse_hostsan"), extra=HOST_SANITIZE)
+    lib = os.path.join(pkg, LIB_NAME)
+    link(objs, lib, extra=["-fsanitize=address", "-fsanitize=undefined"])
+    return lib
 
 
 def build(verbose: bool = False) -> str:
@@ -76,4 +97,7 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose="-q" not in sys.argv)
+    if "--host-sanitize" in sys.argv:
+        print("built", build_host_sanitized(sys.argv[sys.argv.index("--host-sanitize") + 1]))
+    else:
+        build(verbose="-q" not in sys.argv)
