@@ -295,6 +295,12 @@ def test_prefill_argument_checks(U):
     with pytest.raises(U.UocrError) as e:
         U.block_topk_prefill(cfg, (FAKE, need - 1), 0, 100, 64, FAKE, stream=0)
     assert e.value.status == 3
+    # the scoring's limit: 64 splits of at most 512 blocks
+    assert U.workspace_size(cfg, U.OP_INDEXER_PREFILL, 100, 32768) > 0
+    assert U.workspace_size(cfg, U.OP_INDEXER_PREFILL, 100, 32769) == 0
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_prefill(cfg, _kv(U, batch=1, max_blocks=32769), FAKE, 0, 100, (FAKE, 1 << 30), stream=0)
+    assert e.value.status == 5
     big = U.make_cfg(topk_blocks=40)
     with pytest.raises(U.UocrError) as e:
         U.indexer_score_prefill(big, kv1, FAKE, 0, 100, (FAKE, 1 << 30), stream=0)

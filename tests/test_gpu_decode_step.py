@@ -234,6 +234,26 @@ def test_context_above_4096_candidate_blocks():
     oracle_check(wl, res, 1, 0, G.ocfg())
 
 
+def test_maximum_candidate_count():
+    """The largest context the step accepts: max_blocks - local = 16384
+    candidate blocks (a 524,416-token sequence, where every thread of the
+    selection holds its full share of keys) beside a short sequence.  The one
+    launch, the per-layer launches and the separate entry points agree bit
+    for bit on scores and selections, and both sequences match the oracle."""
+    lens = [16388 * 32, 3000]
+    wl = _wl("step maximum candidates", 0x5708, lens, layers=1)
+    print("case: decode step at the candidate limit, max_blocks", wl.max_blocks, flush=True)
+    dev = SD.generate(wl)
+    cfg = G.cfg_for(wl)
+    assert wl.max_blocks - cfg.local_blocks == 16384
+    res = run_step(dev, cfg)
+    assert res["err"] == 0
+    compare_with_separate(dev, cfg, res)
+    compare_with_separate(dev, cfg, run_step(dev, cfg, schedule=U.STEP_PER_LAYER), atol=0)
+    for b in range(wl.batch):
+        oracle_check(wl, res, 0, b, G.ocfg())
+
+
 def test_out_of_range_pool_blocks():
     """Block-table entries outside the pool (-1, >= num_blocks): their blocks
     score NaN, rank last and are never attended, exactly as in the separate

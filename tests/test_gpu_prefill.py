@@ -10,16 +10,17 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
+import block_sparse_long_sr_amd as U  # noqa: E402
 import oracle  # noqa: E402
 from synth import device as SD  # noqa: E402
 from synth import workloads as W  # noqa: E402
 import gpu_harness as G  # noqa: E402
 
 
-def check_prefill(wl, rows, topk=16, local=4, exact=False):
+def check_prefill(wl, rows, topk=16, local=4, exact=False, block_major=True):
     cfg_u, cfg_o = G.cfg_for(wl, topk, local), G.ocfg(topk, local)
     dev = SD.generate(wl)
-    res = G.gpu_prefill(dev, cfg_u)
+    res = G.gpu_prefill(dev, cfg_u, block_major=block_major)
     S = int(wl.ctx_lens[0])
     kidx = wl.kidx(0, 0, 0, S)
     allrows = np.arange(wl.rows)
@@ -36,7 +37,7 @@ def check_prefill(wl, rows, topk=16, local=4, exact=False):
             G.check_selection(res["idx"][t], r, topk)
         assert res["nsel"][t] == min(topk, (wl.q_start + t) // 32 + 1)
         idx_oracle[t] = G.pad_idx(r["selected"], topk)
-    res_o = G.gpu_prefill(dev, cfg_u, idx_override=idx_oracle)
+    res_o = G.gpu_prefill(dev, cfg_u, idx_override=idx_oracle, block_major=block_major)
     for r in refs:
         t = r["row"]
         G.check_attention(res_o["out"][t], res_o["lse"][t], r["out"], r["lse"])
@@ -89,6 +90,20 @@ def test_prefill_full_chunk_sampled():
     print("case:", wl.name, flush=True)
     rows = [0, 1, 31, 32, 511, 512, 1024, 2047] + list(range(7, 2048, 331))
     check_prefill(wl, sorted(set(rows)))
+
+
+def test_prefill_maximum_context():
+    """The longest context the prefill scoring accepts: 32768 blocks (a
+    1,048,576-token context) in 64 splits of 512 blocks, so list entries carry
+    the widest (9-bit) in-split block ids; a ragged 600-row chunk ending at
+    the context's last token.  The attention takes the row-major gather (the
+    block-major workspace covers at most 16384 blocks)."""
+    S = 32768 * 32
+    wl = W.prefill_case("prefill S=1048576 q_start=1047976 T=600", 0xF9, S, S - 600, 600)
+    print("case:", wl.name, flush=True)
+    cfg = G.cfg_for(wl)
+    assert U.workspace_size(cfg, U.OP_ATTN_PREFILL, wl.rows, wl.max_blocks) == 0
+    check_prefill(wl, [0, 1, 31, 32, 299, 511, 512, 599], block_major=False)
 
 
 def test_prefill_nan_key_in_candidate_block_ranks_last():
