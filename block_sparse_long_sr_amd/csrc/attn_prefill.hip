@@ -32,7 +32,8 @@ constexpr int kBucketThreads = 1024;
 constexpr int kBlockWaves = 4;                  // one (chunk, head) per wave
 constexpr int kPStride = 36;                    // P row stride in LDS (floats), padded against bank conflicts
 constexpr int kMergeWaves = 4;
-constexpr int kPairUnroll = 8;                  // pair loads in flight per thread in the bucket pass
+constexpr int kPairUnroll = 32;                 // pairs per thread kept in registers by the bucket pass
+constexpr int kPairTail = 4;                    // pairs per thread and round beyond those
 constexpr int kPartStride = kDim + 4;           // o[128], m, l, pad: 528 B per (row, head, slot)
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -70,32 +71,59 @@ __device__ __forceinline__ int div_by(int i, int d, uint32_t magic) {
 // a contiguous range of blocks), then a scatter through LDS cursors.  The
 // order of pairs inside a bucket is not fixed, and does not need to be: each
 // pair's partial has its own slot.
+//
+// Each thread loads its first kPairUnroll pairs in one round and keeps their
+// blocks (-1 where the slot does not count) in registers for the scatter, so
+// a chunk of up to kBucketThreads * kPairUnroll pairs (2048 rows x 16 slots)
+// reads block_idx once, with one memory round trip; larger chunks load the
+// rest in narrower rounds, once for the counts and again for the scatter.
+template <int N>
+__device__ __forceinline__ void bucket_round(const AttnArgs& A, int i0, int npairs, int topk, uint32_t magic, int M,
+                                             int (&jv)[N]) {
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int i = i0 + u * kBucketThreads;
+    jv[u] = i < npairs ? A.block_idx[i] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int i = i0 + u * kBucketThreads;
+    if (jv[u] >= 0 && !slot_counts(jv[u], A.q_start + div_by(i, topk, magic), M)) jv[u] = -1;
+  }
+}
+
+// CNT bounds max_blocks.  With STAGE > 0 (npairs <= STAGE) the bucketed
+// pairs are first written to LDS and then copied out with coalesced stores:
+// one workgroup scattering 4-byte stores over the whole pairs array touches a
+// separate cache line per lane.
+template <int CNT, int STAGE>
 __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(PrefillAttnArgs a) {
-  __shared__ int32_t s_cnt[kMaxBlocksAttnBucket];
+  __shared__ int32_t s_cnt[CNT];
   __shared__ int32_t s_scan[2][kBucketThreads];
+  __shared__ int32_t s_stage[STAGE > 0 ? STAGE : 1];
   const AttnArgs& A = a.attn;
   const WsView w = ws_view(a);
   const int M = A.max_blocks, topk = A.topk;
   const int tid = threadIdx.x;
+  constexpr int kRound = kBucketThreads * kPairUnroll;
 
-  for (int j = tid; j < M; j += kBucketThreads) s_cnt[j] = 0;
-  __syncthreads();
   // Consecutive lanes take consecutive pairs (slots of a few rows), which keeps
   // same-block LDS atomics within a wave to a few lanes.
   const int npairs = A.nq * topk;
   const uint32_t magic = 0xFFFFFFFFu / (uint32_t)topk;
-  for (int i0 = tid; i0 < npairs; i0 += kBucketThreads * kPairUnroll) {
-    int jv[kPairUnroll];
+  int jf[kPairUnroll];  // the first round's blocks, kept for the scatter
+  bucket_round(A, tid, npairs, topk, magic, M, jf);
+  for (int j = tid; j < M; j += kBucketThreads) s_cnt[j] = 0;
+  __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kPairUnroll; ++u) {
-      const int i = i0 + u * kBucketThreads;
-      jv[u] = i < npairs ? A.block_idx[i] : -1;
-    }
+  for (int u = 0; u < kPairUnroll; ++u)
+    if (jf[u] >= 0) atomicAdd(&s_cnt[jf[u]], 1);
+  for (int i0 = tid + kRound; i0 < npairs; i0 += kBucketThreads * kPairTail) {
+    int jv[kPairTail];
+    bucket_round(A, i0, npairs, topk, magic, M, jv);
 #pragma unroll
-    for (int u = 0; u < kPairUnroll; ++u) {
-      const int i = i0 + u * kBucketThreads;
-      if (jv[u] >= 0 && slot_counts(jv[u], A.q_start + div_by(i, topk, magic), M)) atomicAdd(&s_cnt[jv[u]], 1);
-    }
+    for (int u = 0; u < kPairTail; ++u)
+      if (jv[u] >= 0) atomicAdd(&s_cnt[jv[u]], 1);
   }
   __syncthreads();
 
@@ -134,19 +162,22 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
     w.choff[M] = s_scan[1][kBucketThreads - 1];
   }
   __syncthreads();
-  for (int i0 = tid; i0 < npairs; i0 += kBucketThreads * kPairUnroll) {
-    int jv[kPairUnroll];
+  // Cursor values stay below the number of counted pairs (<= npairs <= STAGE).
+  int32_t* const dst = STAGE > 0 ? s_stage : w.pairs;
 #pragma unroll
-    for (int u = 0; u < kPairUnroll; ++u) {
-      const int i = i0 + u * kBucketThreads;
-      jv[u] = i < npairs ? A.block_idx[i] : -1;
-    }
+  for (int u = 0; u < kPairUnroll; ++u)
+    if (jf[u] >= 0) dst[atomicAdd(&s_cnt[jf[u]], 1)] = tid + u * kBucketThreads;
+  for (int i0 = tid + kRound; i0 < npairs; i0 += kBucketThreads * kPairTail) {
+    int jv[kPairTail];
+    bucket_round(A, i0, npairs, topk, magic, M, jv);
 #pragma unroll
-    for (int u = 0; u < kPairUnroll; ++u) {
-      const int i = i0 + u * kBucketThreads;
-      if (jv[u] >= 0 && slot_counts(jv[u], A.q_start + div_by(i, topk, magic), M))
-        w.pairs[atomicAdd(&s_cnt[jv[u]], 1)] = i;
-    }
+    for (int u = 0; u < kPairTail; ++u)
+      if (jv[u] >= 0) dst[atomicAdd(&s_cnt[jv[u]], 1)] = i0 + u * kBucketThreads;
+  }
+  if constexpr (STAGE > 0) {
+    __syncthreads();
+    const int total = s_scan[0][kBucketThreads - 1];
+    for (int k = tid; k < total; k += kBucketThreads) w.pairs[k] = s_stage[k];
   }
 }
 
@@ -354,7 +385,13 @@ PrefillAttnPlan prefill_attn_plan(int32_t T, int32_t heads, int32_t topk, int32_
 hipError_t launch_attn_prefill_blocks(const PrefillAttnArgs& a, hipStream_t stream) {
   const AttnArgs& A = a.attn;
   if (A.nq == 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_prefill_bucket_kernel, dim3(1), dim3(kBucketThreads), 0, stream, a);
+  // Staged bucketing: counts for up to 4096 blocks (16 KB) and up to 32768
+  // pairs (128 KB) in LDS, beside the 8 KB scan.
+  if (A.max_blocks <= 4096 && (int64_t)A.nq * A.topk <= 32768)
+    hipLaunchKernelGGL((attn_prefill_bucket_kernel<4096, 32768>), dim3(1), dim3(kBucketThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_prefill_bucket_kernel<kMaxBlocksAttnBucket, 0>), dim3(1), dim3(kBucketThreads), 0,
+                       stream, a);
   const int64_t units = (int64_t)a.plan.max_chunks * A.heads;
   hipLaunchKernelGGL(attn_prefill_block_kernel, dim3((unsigned)((units + kBlockWaves - 1) / kBlockWaves)),
                      dim3(kBlockWaves * kWave), 0, stream, a);

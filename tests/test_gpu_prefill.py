@@ -92,6 +92,18 @@ def test_prefill_full_chunk_sampled():
     check_prefill(wl, sorted(set(rows)))
 
 
+def test_prefill_block_major_unstaged_bucketing():
+    """A chunk past the bucketing's LDS staging (more than 4096 blocks and
+    more than 32768 (row, slot) pairs): the pairs are scattered straight to
+    the workspace, and those past the first 32768 are loaded in later rounds
+    (rows 2048 and up).  Sampled rows, both sides of that split, against the
+    oracle."""
+    wl = W.prefill_case("prefill S=140000 q_start=137900 T=2100", 0xFA, 140000, 137900, 2100)
+    print("case:", wl.name, flush=True)
+    assert wl.max_blocks > 4096 and wl.rows * 16 > 32768
+    check_prefill(wl, sorted(set([0, 1, 31, 2047, 2048, 2049, 2080, 2099] + list(range(5, 2100, 233)))))
+
+
 def test_prefill_maximum_context():
     """The longest context the prefill scoring accepts: 32768 blocks (a
     1,048,576-token context) in 64 splits of 512 blocks, so list entries carry
