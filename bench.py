@@ -217,6 +217,46 @@ def run_prefill(U, SD, W, torch, iters=5):
     return res
 
 
+def run_short_contexts(U, SD, W, torch, reps=50):
+    """The whole decode step at the two short configurations: one 2048-token
+    sequence with one layer, and 16 sequences x 12 layers at 32768 tokens;
+    per-layer launches, the one launch and the automatic choice, each timed
+    with one event pair around back-to-back steps on one stream."""
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    res = {}
+    for wl in (W.config1(), W.config2()):
+        dev = SD.generate(wl)
+        cfg = U.make_cfg()
+        nl, B, M, H, D = dev.q.shape[0], wl.batch, wl.max_blocks, wl.heads, wl.head_dim
+        kv = U.make_kv(dev.k[0], dev.v[0], dev.kidx[0], dev.block_table, dev.ctx_lens, wl.pool_blocks, B, M)
+        scores = torch.empty((nl, B, M), dtype=torch.float32, device="cuda")
+        idx = torch.empty((nl, B, cfg.topk_blocks), dtype=torch.int32, device="cuda")
+        out = torch.empty((nl, B, H, D), dtype=torch.float32, device="cuda")
+        lse = torch.empty((nl, B, H), dtype=torch.float32, device="cuda")
+        ws = torch.empty(U.workspace_size(cfg, U.OP_DECODE_STEP, nl * B, M), dtype=torch.uint8, device="cuda")
+        us = {}
+        for name, sched in (("per_layer", U.STEP_PER_LAYER), ("one_launch", U.STEP_ONE_LAUNCH), ("auto", U.STEP_AUTO)):
+            def step():
+                U.sparse_decode_step(cfg, kv, nl, dev.q_idx, dev.q, scores, idx, out, lse, ws=ws, stream=sh,
+                                     schedule=sched)
+            for _ in range(5):
+                step()
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a_.record(stream)
+            for _ in range(reps):
+                step()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            us[name] = a_.elapsed_time(b_) / reps * 1e3
+        res[wl.name] = {"layers": nl, "batch": B, "ctx_len": int(wl.ctx_lens.max()), "us_per_step": us,
+                        "query_heads_per_s": {k: nl * B * H / (v * 1e-6) for k, v in us.items()}}
+        del dev, kv, scores, idx, out, lse, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def run_page_gate(U, SD, W, torch, reps=20):
     """Page-aware ranking on the multi-page workloads: the ragged decode batch
     (64 documents of 400 image + 600 text tokens per page, query on the last
@@ -410,6 +450,8 @@ def main():
     ap.add_argument("--no-page-gate", action="store_true", help="skip the page-aware ranking measurement")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense full-context comparator")
     ap.add_argument("--no-rope", action="store_true", help="skip the page2d cache-write measurement")
+    ap.add_argument("--no-short", action="store_true",
+                    help="skip the short-context step timings (one 2048-token query; 16 x 12 layers at 32K)")
     ap.add_argument("--no-layout", action="store_true",
                     help="skip the decode step on the contiguous block layout")
     ap.add_argument("--prefill-only", action="store_true",
@@ -730,6 +772,13 @@ def main():
             f"one launch {pg['decode']['us']['one_launch_page_aware']:.1f} us (plain {pg['decode']['us']['one_launch_plain']:.1f} us); "
             f"prefill scoring+merge {pg['prefill_scoring_and_merge']['us']['page_aware']:.1f} us "
             f"(plain {pg['prefill_scoring_and_merge']['us']['plain']:.1f} us)")
+
+    if not args.no_short:
+        result["short_context"] = run_short_contexts(U, SD, W, torch)
+        for k, v in result["short_context"].items():
+            u = v["us_per_step"]
+            log(f"{k}: per-layer launches {u['per_layer']:.1f} us, one launch {u['one_launch']:.1f} us, "
+                f"automatic {u['auto']:.1f} us per step")
 
     if not args.no_rope:
         result["page2d_rope_cache_write"] = run_rope(U, torch)
