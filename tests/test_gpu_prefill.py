@@ -92,6 +92,31 @@ def test_prefill_full_chunk_sampled():
     check_prefill(wl, sorted(set(rows)))
 
 
+def test_prefill_attention_hot_blocks():
+    """Every row of a 2048-row chunk keeps the same 16 blocks: each bucket
+    holds 2048 pairs (64 full 32-row chunks of one block), the staged
+    bucketing's LDS counters take 2048 atomics each, and most blocks get no
+    pair at all.  Block-major against row-major and sampled rows against the
+    oracle."""
+    wl = W.prefill_case("prefill hot blocks S=8192 q_start=6144 T=2048", 0xFB, 8192, 6144, 2048)
+    print("case:", wl.name, flush=True)
+    cfg_u, cfg_o = G.cfg_for(wl), G.ocfg()
+    dev = SD.generate(wl)
+    T = wl.rows
+    hot = np.array([0, 3, 17, 40, 41, 42, 99, 100, 150, 151, 152, 160, 170, 180, 190, 191], np.int32)
+    idx = np.tile(hot, (T, 1))
+    res_b = G.gpu_prefill(dev, cfg_u, idx_override=idx)
+    res_r = G.gpu_prefill(dev, cfg_u, idx_override=idx, block_major=False)
+    assert np.abs(res_b["out"] - res_r["out"]).max() <= 1e-5
+    assert np.abs(res_b["lse"] - res_r["lse"]).max() <= 1e-5
+    q = wl.q_rows(np.arange(T))
+    toks = np.concatenate([oracle.attended_tokens([int(j)], wl.q_start, cfg_o) for j in hot])
+    k_, v_ = G.fetcher(wl, 0, 0)(toks)
+    for t in [0, 1, 31, 32, 1000, 2047]:
+        o2, l2 = oracle.attend(q[t], k_, v_, np.arange(toks.size), cfg_o.sm_scale)
+        G.check_attention(res_b["out"][t], res_b["lse"][t], o2, l2)
+
+
 def test_prefill_block_major_unstaged_bucketing():
     """A chunk past the bucketing's LDS staging (more than 4096 blocks and
     more than 32768 (row, slot) pairs): the pairs are scattered straight to
