@@ -234,6 +234,25 @@ def test_context_above_4096_candidate_blocks():
     oracle_check(wl, res, 1, 0, G.ocfg())
 
 
+@pytest.mark.parametrize("batch,layers", [(200, 3), (3, 5)])
+def test_batch_shapes(batch, layers):
+    """Ticket order at other batch sizes: 200 sequences (lag 100, 600 slots)
+    and 3 sequences (lag 1), ragged contexts of 1 to 6000 tokens, forced to
+    the one launch: no wait gives up, scores and selections equal the
+    separate launches bit for bit, sampled queries match the oracle."""
+    g = np.random.default_rng(0x5709 + batch)
+    lens = g.integers(1, 6000, size=batch)
+    wl = _wl(f"step batch {batch} x {layers} layers", 0x5709 + batch, lens, layers=layers)
+    print(f"case: decode step batch {batch} x {layers} layers", flush=True)
+    dev = SD.generate(wl)
+    cfg = G.cfg_for(wl)
+    res = run_step(dev, cfg)
+    assert res["err"] == 0
+    compare_with_separate(dev, cfg, res)
+    for layer, b in ((0, 0), (layers - 1, batch - 1), (layers // 2, batch // 2)):
+        oracle_check(wl, res, layer, b, G.ocfg())
+
+
 def test_maximum_candidate_count():
     """The largest context the step accepts: max_blocks - local = 16384
     candidate blocks (a 524,416-token sequence, where every thread of the
