@@ -92,12 +92,15 @@ __device__ __forceinline__ void bucket_round(const AttnArgs& A, int i0, int npai
   }
 }
 
-// CNT bounds max_blocks.  With STAGE > 0 (npairs <= STAGE) the bucketed
-// pairs are first written to LDS and then copied out with coalesced stores:
-// one workgroup scattering 4-byte stores over the whole pairs array touches a
-// separate cache line per lane.
+// CNT bounds max_blocks.  With STAGE > 0 (npairs <= STAGE, so every pair is
+// in the first round) the counting atomics return each pair's rank in its
+// bucket, the pairs go to bucket start + rank in an LDS copy of the pairs
+// array without a second round of atomics, and that copy is written out with
+// coalesced stores: one workgroup scattering 4-byte stores over the whole
+// pairs array touches a separate cache line per lane.
 template <int CNT, int STAGE>
 __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(PrefillAttnArgs a) {
+  static_assert(STAGE <= kBucketThreads * kPairUnroll, "staged pairs must all be in the first round");
   __shared__ int32_t s_cnt[CNT];
   __shared__ int32_t s_scan[2][kBucketThreads];
   __shared__ int32_t s_stage[STAGE > 0 ? STAGE : 1];
@@ -115,15 +118,23 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
   bucket_round(A, tid, npairs, topk, magic, M, jf);
   for (int j = tid; j < M; j += kBucketThreads) s_cnt[j] = 0;
   __syncthreads();
+  int rk[kPairUnroll];  // STAGE > 0: each pair's rank in its bucket
 #pragma unroll
-  for (int u = 0; u < kPairUnroll; ++u)
-    if (jf[u] >= 0) atomicAdd(&s_cnt[jf[u]], 1);
-  for (int i0 = tid + kRound; i0 < npairs; i0 += kBucketThreads * kPairTail) {
-    int jv[kPairTail];
-    bucket_round(A, i0, npairs, topk, magic, M, jv);
+  for (int u = 0; u < kPairUnroll; ++u) {
+    if constexpr (STAGE > 0) {
+      rk[u] = jf[u] >= 0 ? atomicAdd(&s_cnt[jf[u]], 1) : 0;
+    } else {
+      if (jf[u] >= 0) atomicAdd(&s_cnt[jf[u]], 1);
+    }
+  }
+  if constexpr (STAGE == 0) {
+    for (int i0 = tid + kRound; i0 < npairs; i0 += kBucketThreads * kPairTail) {
+      int jv[kPairTail];
+      bucket_round(A, i0, npairs, topk, magic, M, jv);
 #pragma unroll
-    for (int u = 0; u < kPairTail; ++u)
-      if (jv[u] >= 0) atomicAdd(&s_cnt[jv[u]], 1);
+      for (int u = 0; u < kPairTail; ++u)
+        if (jv[u] >= 0) atomicAdd(&s_cnt[jv[u]], 1);
+    }
   }
   __syncthreads();
 
@@ -162,22 +173,26 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
     w.choff[M] = s_scan[1][kBucketThreads - 1];
   }
   __syncthreads();
-  // Cursor values stay below the number of counted pairs (<= npairs <= STAGE).
-  int32_t* const dst = STAGE > 0 ? s_stage : w.pairs;
-#pragma unroll
-  for (int u = 0; u < kPairUnroll; ++u)
-    if (jf[u] >= 0) dst[atomicAdd(&s_cnt[jf[u]], 1)] = tid + u * kBucketThreads;
-  for (int i0 = tid + kRound; i0 < npairs; i0 += kBucketThreads * kPairTail) {
-    int jv[kPairTail];
-    bucket_round(A, i0, npairs, topk, magic, M, jv);
-#pragma unroll
-    for (int u = 0; u < kPairTail; ++u)
-      if (jv[u] >= 0) dst[atomicAdd(&s_cnt[jv[u]], 1)] = i0 + u * kBucketThreads;
-  }
   if constexpr (STAGE > 0) {
+    // s_cnt now holds each bucket's first position; start + rank stays below
+    // the number of counted pairs (<= npairs <= STAGE).
+#pragma unroll
+    for (int u = 0; u < kPairUnroll; ++u)
+      if (jf[u] >= 0) s_stage[s_cnt[jf[u]] + rk[u]] = tid + u * kBucketThreads;
     __syncthreads();
     const int total = s_scan[0][kBucketThreads - 1];
     for (int k = tid; k < total; k += kBucketThreads) w.pairs[k] = s_stage[k];
+  } else {
+#pragma unroll
+    for (int u = 0; u < kPairUnroll; ++u)
+      if (jf[u] >= 0) w.pairs[atomicAdd(&s_cnt[jf[u]], 1)] = tid + u * kBucketThreads;
+    for (int i0 = tid + kRound; i0 < npairs; i0 += kBucketThreads * kPairTail) {
+      int jv[kPairTail];
+      bucket_round(A, i0, npairs, topk, magic, M, jv);
+#pragma unroll
+      for (int u = 0; u < kPairTail; ++u)
+        if (jv[u] >= 0) w.pairs[atomicAdd(&s_cnt[jv[u]], 1)] = i0 + u * kBucketThreads;
+    }
   }
 }
 
