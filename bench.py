@@ -460,7 +460,7 @@ def main():
                     help="only copy 1 GiB device-to-device 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the decode step shards by sequence with no communication across GPUs)", file=sys.stderr)
         sys.exit(2)
 
