@@ -148,6 +148,13 @@ def cpu_baseline(dev, wl, n_layers, passes=2):
     return nq, total
 
 
+def prefill_flops(wl, local=4):
+    """Algorithmic work of the prefill scoring kernel: a 128-dim bf16 dot
+    product (2 x 128 FLOP) for every key of every candidate (row, block)."""
+    rowblocks = sum(max(0, (wl.q_start + t) // 32 + 1 - local) for t in range(wl.rows))
+    return rowblocks * 32 * 128 * 2
+
+
 def run_prefill(U, SD, W, torch, iters=5):
     wl = W.config5()
     dev = SD.generate(wl)
@@ -194,9 +201,7 @@ def run_prefill(U, SD, W, torch, iters=5):
     torch.cuda.synchronize()
     batches = [a_.elapsed_time(b_) / nrep for a_, b_ in bev]
     t_sc_alone = sorted(batches)[nbatch // 2]
-    # algorithmic work of the scoring kernel: every candidate (row, block) pair
-    rowblocks = sum(max(0, (wl.q_start + t) // 32 + 1 - 4) for t in range(T))
-    flops = rowblocks * 32 * 128 * 2
+    flops = prefill_flops(wl)
     tflops = flops / (t_sc_alone * 1e-3) / 1e12
     attn_unique = int(wl.ctx_lens[0]) * 10 * 128 * 2 * 2
     res = {

@@ -45,6 +45,16 @@ def test_headline_step_bytes():
     assert sum(_bench().decode_bytes(wl)) * wl.layers == total
 
 
+def test_prefill_chunk_flops():
+    """2048 rows at offset 129024 of a 131072-token context: each row scores
+    the 32 keys of each of its candidate blocks with a 128-dim dot product."""
+    wl = W.config5()
+    cfg = oracle.SparseCfg()
+    flops = sum(oracle.candidate_count(wl.q_start + t, cfg) * cfg.block_size * 128 * 2 for t in range(wl.rows))
+    assert flops == 68_123_885_568
+    assert _bench().prefill_flops(wl) == flops
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120, cwd=ROOT)
