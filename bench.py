@@ -102,50 +102,265 @@ def traffic_for(kernel):
     return int(float(rec["hbm_bytes_per_launch"]))
 
 
-def cpu_baseline(dev, wl, n_layers, passes=2):
-    """Time the CPU oracle on (16 sequences x n_layers) decode queries of the
-    same workload, each computed `passes` times (about 10 s of CPU work for
-    the whole step).  Inputs are copied from device memory beforehand; the
-    time spent gathering K/V rows for the oracle is excluded."""
+def host_description():
+    """The host the CPU oracle runs on: CPU model, cores this process may
+    use, and the BLAS library numpy calls with its thread count."""
+    from threadpoolctl import threadpool_info
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [{"library": d.get("internal_api"), "version": d.get("version"), "threads": d.get("num_threads")}
+            for d in threadpool_info() if d.get("user_api") == "blas"]
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(),
+            "blas": blas}
+
+
+# Parity rule of the decode path against the oracle (the same rule the GPU
+# tests apply): selections equal except blocks whose oracle score lies within
+# 1e-4 relative of the cutoff (equal sizes, local blocks kept); attention
+# max-abs <= 2e-3 and relative L2 <= 1e-3 per query, lse within 1e-4.
+BAND, ATT_MAX_ABS, ATT_REL_L2, LSE_ABS = 1e-4, 2e-3, 1e-3, 1e-4
+
+
+class ParityTally:
+    """Per-query comparison of GPU selections and attention outputs with the
+    oracle's, accumulated into the bench record."""
+
+    def __init__(self):
+        self.queries = 0
+        self.exact = 0
+        self.in_band = 0
+        self.outside_band = 0
+        self.failures = []
+        self.att = {"max_abs": 0.0, "rel_l2": 0.0, "lse_abs": 0.0}
+        self.att_oracle_set = {"max_abs": 0.0, "rel_l2": 0.0, "lse_abs": 0.0}
+
+    @staticmethod
+    def _errors(out, lse, ref_out, ref_lse):
+        import numpy as np
+        g = out.astype(np.float64)
+        err = float(np.abs(g - ref_out).max()) if g.size else 0.0
+        nrm = float(np.linalg.norm(ref_out))
+        rel = float(np.linalg.norm(g - ref_out) / nrm) if nrm > 0 else float(np.linalg.norm(g))
+        fin = np.isfinite(ref_lse)
+        lerr = float(np.abs(lse[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
+        if not np.all(np.isneginf(lse[~fin])) or not np.all(np.isfinite(g)):
+            lerr = float("inf")
+        return err, rel, lerr
+
+    def _attention(self, key, where, out, lse, ref_out, ref_lse):
+        err, rel, lerr = self._errors(out, lse, ref_out, ref_lse)
+        acc = self.att if key == "gpu" else self.att_oracle_set
+        acc["max_abs"] = max(acc["max_abs"], err)
+        acc["rel_l2"] = max(acc["rel_l2"], rel)
+        acc["lse_abs"] = max(acc["lse_abs"], lerr)
+        if not (err <= ATT_MAX_ABS and rel <= ATT_REL_L2 and lerr <= LSE_ABS):
+            self.failures.append(f"{where}: attention ({key} set) max-abs {err:.2e} rel-L2 {rel:.2e} lse {lerr:.2e}")
+
+    def add(self, where, ref, idx_row, out, lse, q, fetch, p, cfg_o):
+        """One query: ``ref`` is the oracle's result; the GPU's selection
+        ``idx_row`` and its attention on that selection (out, lse)."""
+        import numpy as np
+        import oracle
+        self.queries += 1
+        got = [int(x) for x in idx_row if x >= 0]
+        want = ref["selected"]
+        band = set()
+        if ref["cutoff"] is not None:
+            c = ref["cutoff"]
+            band = set(np.nonzero(np.abs(ref["block_scores"].astype(np.float64) - c) <= BAND * abs(c))[0].tolist())
+        well_formed = (got == sorted(got) and list(idx_row[len(got):]) == [-1] * (len(idx_row) - len(got))
+                       and len(got) == len(want) and all(j in got for j in ref["local"]))
+        if got == want:
+            self.exact += 1
+            self._attention("gpu", where, out, lse, ref["out"], ref["lse"])
+        elif well_formed and set(got) - band == set(want) - band:
+            self.in_band += 1
+            toks = oracle.attended_tokens(got, p, cfg_o)
+            k, v = fetch(toks)
+            o2, l2 = oracle.attend(q, k, v, np.arange(toks.size), cfg_o.sm_scale)
+            self._attention("gpu", where, out, lse, o2, l2)
+        else:
+            self.outside_band += 1
+            self.failures.append(f"{where}: selection gpu {got} oracle {want}")
+
+    def add_oracle_set(self, where, out, lse, ref_out, ref_lse):
+        """The GPU's attention run on the oracle's own index set."""
+        self._attention("oracle", where, out, lse, ref_out, ref_lse)
+
+    def record(self):
+        return {"queries": self.queries, "selection_exact": self.exact,
+                "selection_differences_inside_band": self.in_band,
+                "selection_mismatches_outside_band": self.outside_band,
+                "attention_on_gpu_selection": self.att, "attention_on_oracle_selection": self.att_oracle_set,
+                "tolerance": {"band_rel": BAND, "max_abs": ATT_MAX_ABS, "rel_l2": ATT_REL_L2, "lse_abs": LSE_ABS},
+                "pass": not self.failures, "failures": self.failures[:8]}
+
+
+def cpu_baseline(U, dev, wl, n_layers, gpu, cfg):
+    """The CPU oracle on every (layer, sequence) query of the step, on the
+    device inputs copied to the host: once with numpy's BLAS on all its
+    threads (results kept) and once on one thread; the time spent copying
+    inputs and fetching K/V rows is excluded.  The kept results are then
+    compared with the GPU's outputs of the timed step (``gpu``: host copies
+    of idx [L][B][topk], out [L][B][H][D], lse [L][B][H]), and the GPU's
+    attention is run once more on the oracle's own index sets.  Returns
+    (timing, parity record)."""
     import numpy as np
     import torch
     import oracle
     from threadpoolctl import threadpool_limits
 
-    tab = dev.block_table
-    B, L = wl.batch, wl.ctx_lens
-    total = 0.0
+    cfg_o = oracle.SparseCfg()
+    B, H = wl.batch, wl.heads
+    topk = cfg_o.topk_blocks
+    t_all = t_one = 0.0
     nq = 0
-    with threadpool_limits(limits=1):
-        for l in range(n_layers):
-            for b in range(B):
-                S = int(L[b])
-                nb = -(-S // 32)
-                blocks = tab[b, :nb].long()
-                ki = dev.kidx[l].index_select(0, blocks).reshape(nb * 32, -1)[:S]
-                ki = ki.cpu().numpy().view(np.uint16)
-                q = dev.q[l, b].cpu().numpy().view(np.uint16)
-                qi = dev.q_idx[l, b].cpu().numpy().view(np.uint16)
-                fetch_time = [0.0]
+    tally = ParityTally()
+    idx_o = np.full((n_layers, B, topk), -1, np.int32)
+    ref_att = {}
+    for l in range(n_layers):
+        for b in range(B):
+            L = int(wl.ctx_lens[b])
+            kidx = dev.host_kidx(l, b, L)
+            q, qi = dev.host_decode_queries(l, b)
+            base_fetch = dev.host_kv_fetch(l, b)
+            fetch_time = [0.0]
 
-                def fetch(toks, l=l, b=b):
-                    t0 = time.perf_counter()
-                    pb = tab[b, torch.from_numpy(toks // 32).to(tab.device)].long()
-                    off = torch.from_numpy(toks % 32).to(tab.device)
-                    k = dev.k[l].index_select(0, pb)[torch.arange(len(toks), device=tab.device), :, off, :]
-                    v = dev.v[l].index_select(0, pb)[torch.arange(len(toks), device=tab.device), :, off, :]
-                    r = (k.transpose(0, 1).contiguous().cpu().numpy().view(np.uint16),
-                         v.transpose(0, 1).contiguous().cpu().numpy().view(np.uint16))
-                    fetch_time[0] += time.perf_counter() - t0
-                    return r
+            def fetch(toks):
+                t0 = time.perf_counter()
+                r = base_fetch(toks)
+                fetch_time[0] += time.perf_counter() - t0
+                return r
 
-                for _ in range(passes):
-                    fetch_time[0] = 0.0
-                    t0 = time.perf_counter()
-                    oracle.decode_query_fetch(q, qi, ki, fetch, S)
-                    total += time.perf_counter() - t0 - fetch_time[0]
-                    nq += 1
-    return nq, total
+            fetch_time[0] = 0.0
+            t0 = time.perf_counter()
+            ref = oracle.decode_query_fetch(q, qi, kidx, fetch, L, cfg_o)
+            t_all += time.perf_counter() - t0 - fetch_time[0]
+            with threadpool_limits(limits=1):
+                fetch_time[0] = 0.0
+                t0 = time.perf_counter()
+                oracle.decode_query_fetch(q, qi, kidx, fetch, L, cfg_o)
+                t_one += time.perf_counter() - t0 - fetch_time[0]
+            nq += 1
+            tally.add(f"layer {l} seq {b}", ref, gpu["idx"][l, b], gpu["out"][l, b], gpu["lse"][l, b], q,
+                      base_fetch, L - 1, cfg_o)
+            idx_o[l, b, :len(ref["selected"])] = ref["selected"]
+            ref_att[(l, b)] = (ref["out"], ref["lse"])
+    out2 = torch.empty((B, H, 128), dtype=torch.float32, device="cuda")
+    lse2 = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    for l in range(n_layers):
+        U.sparse_attn_decode(cfg, dev.kv(l), dev.q[l], torch.from_numpy(idx_o[l]).cuda(), out2, lse2)
+        o, s = out2.cpu().numpy(), lse2.cpu().numpy()
+        for b in range(B):
+            tally.add_oracle_set(f"layer {l} seq {b}", o[b], s[b], *ref_att[(l, b)])
+    return {"queries": nq, "seconds_all_threads": t_all, "seconds_one_thread": t_one}, tally.record()
+
+
+def micro_batch_step(U, torch, dev, cfg, bufs, n_groups, separate=False, base=None):
+    """The decode step as per-layer launches over micro-batches: the batch is
+    split into ``n_groups`` groups of sequences, each running its layers in
+    order on its own HIP stream (default priority), so that one group's
+    latency-bound selection + attention overlaps another group's
+    bandwidth-bound scoring.  Each group calls the entry points on views of
+    the batch (descriptor pointers offset by the group's first sequence).
+    Returns (step, fork, join): fork(base) makes the group streams wait for
+    ``base``, join(base) makes ``base`` wait for them.  With one group and
+    ``base`` given, that group runs on ``base`` itself."""
+    wl = dev.wl
+    B, M, L = wl.batch, wl.max_blocks, dev.q.shape[0]
+    scores, idx, out, lse = bufs
+    ns = max(1, min(n_groups, B))
+    bounds = [(B * i) // ns for i in range(ns + 1)]
+    groups = []
+    for i in range(ns):
+        b0, b1 = bounds[i], bounds[i + 1]
+        gkv = [U.make_kv(dev.k[l], dev.v[l], dev.kidx[l], dev.block_table[b0:b1], dev.ctx_lens[b0:b1],
+                         wl.pool_blocks, b1 - b0, M) for l in range(L)]
+        groups.append((b0, b1, gkv, base if (ns == 1 and base is not None) else torch.cuda.Stream()))
+
+    def step():
+        for l in range(L):
+            for b0, b1, gkv, st in groups:
+                h_ = st.cuda_stream
+                U.indexer_score_decode(cfg, gkv[l], dev.q_idx[l, b0:b1], scores[l, b0:b1], stream=h_)
+                if separate:
+                    U.block_topk_decode(cfg, scores[l, b0:b1], dev.ctx_lens[b0:b1], b1 - b0, M, idx[l, b0:b1],
+                                        stream=h_)
+                    U.sparse_attn_decode(cfg, gkv[l], dev.q[l, b0:b1], idx[l, b0:b1], out[l, b0:b1],
+                                         lse[l, b0:b1], stream=h_)
+                else:
+                    U.topk_attn_decode(cfg, gkv[l], dev.q[l, b0:b1], scores[l, b0:b1], idx[l, b0:b1],
+                                       out[l, b0:b1], lse[l, b0:b1], stream=h_)
+
+    def fork(base_):
+        ev = torch.cuda.Event()
+        ev.record(base_)
+        for _, _, _, st in groups:
+            if st is not base_:
+                st.wait_event(ev)
+
+    def join(base_):
+        for _, _, _, st in groups:
+            if st is not base_:
+                ev = torch.cuda.Event()
+                ev.record(st)
+                base_.wait_event(ev)
+
+    return step, fork, join
+
+
+def time_steps(torch, stream, step, reps, warmup, fork=None, join=None):
+    """Average duration (ms) of ``reps`` back-to-back steps after ``warmup``
+    untimed ones: one event pair on ``stream`` around the whole run."""
+    fork = fork or (lambda b: None)
+    join = join or (lambda b: None)
+    fork(stream)
+    for _ in range(warmup):
+        step()
+    join(stream)
+    torch.cuda.synchronize()
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_.record(stream)
+    fork(stream)
+    for _ in range(reps):
+        step()
+    join(stream)
+    b_.record(stream)
+    torch.cuda.synchronize()
+    return a_.elapsed_time(b_) / reps
+
+
+def schedule_timings(U, torch, dev, cfg, bufs, step_ws, reps, warmup, step_bytes):
+    """The same decode step under each schedule, on the same inputs: the one
+    launch (every layer's queries given before it starts), per-layer
+    launches on one stream, and per-layer launches over two micro-batch
+    streams.  The per-layer schedules need each layer's queries only when
+    that layer starts, as a model produces them."""
+    wl = dev.wl
+    B, L, H = wl.batch, dev.q.shape[0], wl.heads
+    scores, idx, out, lse = bufs
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    kv0 = dev.kv(0)
+    res = {}
+
+    def lib_step(sched):
+        return lambda: U.sparse_decode_step(cfg, kv0, L, dev.q_idx, dev.q, scores, idx, out, lse, ws=step_ws,
+                                            stream=sh, schedule=sched)
+
+    res["one_launch"] = time_steps(torch, stream, lib_step(U.STEP_ONE_LAUNCH), reps, warmup)
+    res["per_layer_one_stream"] = time_steps(torch, stream, lib_step(U.STEP_PER_LAYER), reps, warmup)
+    st2, fk, jn = micro_batch_step(U, torch, dev, cfg, bufs, 2)
+    res["per_layer_two_streams"] = time_steps(torch, stream, st2, reps, warmup, fk, jn)
+    return {k: {"us_per_step": v * 1e3, "query_heads_per_s": B * L * H / (v * 1e-3),
+                "hbm_frac": step_bytes / (v * 1e-3) / 1e9 / HBM_PEAK_GBPS} for k, v in res.items()}
 
 
 def prefill_flops(wl, local=4):
@@ -245,18 +460,16 @@ def run_short_contexts(U, SD, W, torch, reps=50):
             def step():
                 U.sparse_decode_step(cfg, kv, nl, dev.q_idx, dev.q, scores, idx, out, lse, ws=ws, stream=sh,
                                      schedule=sched)
-            for _ in range(5):
-                step()
-            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            a_.record(stream)
-            for _ in range(reps):
-                step()
-            b_.record(stream)
-            torch.cuda.synchronize()
-            us[name] = a_.elapsed_time(b_) / reps * 1e3
+            us[name] = time_steps(torch, stream, step, reps, 5) * 1e3
+        if B >= 2:
+            st2, fk, jn = micro_batch_step(U, torch, dev, cfg, (scores, idx, out, lse), 2)
+            us["per_layer_two_streams"] = time_steps(torch, stream, st2, reps, 5, fk, jn) * 1e3
+        idx_b, topk_b, attn_b = decode_bytes(wl)
+        step_bytes = nl * (idx_b + topk_b + attn_b)
         res[wl.name] = {"layers": nl, "batch": B, "ctx_len": int(wl.ctx_lens.max()), "us_per_step": us,
-                        "query_heads_per_s": {k: nl * B * H / (v * 1e-6) for k, v in us.items()}}
+                        "query_heads_per_s": {k: nl * B * H / (v * 1e-6) for k, v in us.items()},
+                        "step_algorithmic_bytes": step_bytes,
+                        "hbm_frac": {k: step_bytes / (v * 1e-6) / 1e9 / HBM_PEAK_GBPS for k, v in us.items()}}
         del dev, kv, scores, idx, out, lse, ws
         torch.cuda.empty_cache()
     return res
@@ -451,6 +664,9 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=12,
                     help="layers of the workload the CPU oracle is timed on (x16 queries)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-schedules", action="store_true",
+                    help="skip timing the step under the other schedules (one launch, per-layer on one and on two "
+                         "streams)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-page-gate", action="store_true", help="skip the page-aware ranking measurement")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense full-context comparator")
@@ -508,64 +724,27 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    # Micro-batches: the sequences are independent, so the batch is split into
-    # `streams` groups, each running its 12 layers in order on its own stream;
-    # one group's latency-bound selection/attention overlaps another group's
-    # bandwidth-bound scoring.  Each group uses the same entry points on views
-    # of the batch (descriptor pointers offset by the group's first sequence).
-    ns = max(1, min(args.streams, B))
-    bounds = [(B * i) // ns for i in range(ns + 1)]
-    groups = []
-    for i in range(ns):
-        b0, b1 = bounds[i], bounds[i + 1]
-        gkv = []
-        for l in range(L):
-            gkv.append(U.make_kv(dev.k[l], dev.v[l], dev.kidx[l], dev.block_table[b0:b1], dev.ctx_lens[b0:b1],
-                                 wl.pool_blocks, b1 - b0, M))
-        groups.append((b0, b1, gkv, torch.cuda.Stream() if ns > 1 or args.graph else stream))
-
     one_launch = not args.multi_launch
     step_ws = None
+    step_ws_sched = torch.empty(U.workspace_size(cfg, U.OP_DECODE_STEP, L * B, M), dtype=torch.uint8, device="cuda")
     if one_launch:
         wsb = U.workspace_size(cfg, U.OP_DECODE_STEP, L * B, M)
         step_ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
         kv0 = dev.kv(0)
+        fork = join = lambda base: None
 
-    def step():
-        if one_launch:
+        def step():
             U.sparse_decode_step(cfg, kv0, L, dev.q_idx, dev.q, scores, idx, out, lse, ws=step_ws, stream=sh,
                                  schedule=U.STEP_ONE_LAUNCH)
-            return
-        for l in range(L):
-            for b0, b1, gkv, st in groups:
-                h_ = st.cuda_stream
-                U.indexer_score_decode(cfg, gkv[l], dev.q_idx[l, b0:b1], scores[l, b0:b1], stream=h_)
-                if args.separate:
-                    U.block_topk_decode(cfg, scores[l, b0:b1], dev.ctx_lens[b0:b1], b1 - b0, M, idx[l, b0:b1],
-                                        stream=h_)
-                    U.sparse_attn_decode(cfg, gkv[l], dev.q[l, b0:b1], idx[l, b0:b1], out[l, b0:b1],
-                                         lse[l, b0:b1], stream=h_)
-                else:
-                    U.topk_attn_decode(cfg, gkv[l], dev.q[l, b0:b1], scores[l, b0:b1], idx[l, b0:b1],
-                                       out[l, b0:b1], lse[l, b0:b1], stream=h_)
-
-    def fork(base):
-        ev = torch.cuda.Event()
-        ev.record(base)
-        for _, _, _, st in groups:
-            if st is not base:
-                st.wait_event(ev)
-
-    def join(base):
-        for _, _, _, st in groups:
-            if st is not base:
-                ev = torch.cuda.Event()
-                ev.record(st)
-                base.wait_event(ev)
+    else:
+        step, fork, join = micro_batch_step(U, torch, dev, cfg, (scores, idx, out, lse), args.streams,
+                                            separate=args.separate, base=None if args.graph else stream)
 
     fork(stream)
     for _ in range(args.warmup):
         step()
+        if step_ws is not None:
+            U.check_decode_step(step_ws)   # every warm-up step: no dependency wait gave up
     join(stream)
     torch.cuda.synchronize()
     graph = None
@@ -597,8 +776,10 @@ def main():
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / args.steps
-    if step_ws is not None and int(step_ws[4:8].cpu().numpy().view(np.uint32)[0]) != 0:
-        raise RuntimeError("a dependency wait of the one-launch decode step gave up")
+    if step_ws is not None:
+        U.check_decode_step(step_ws)   # the last timed step (each call clears the word first)
+    # the timed step's outputs, kept for the parity check against the oracle
+    gpu_out = {"idx": idx.cpu().numpy(), "out": out.cpu().numpy(), "lse": lse.cpu().numpy()}
     qh_per_s = B * L * H * args.steps / (ms_total * 1e-3)
     log(f"decode step {ms_step * 1e3:.1f} us, {qh_per_s / 1e6:.3f} M query-heads/s")
 
@@ -661,7 +842,7 @@ def main():
                    "heads": H, "head_dim": 128, "block_size": 32, "topk_blocks": 16, "local_blocks": 4,
                    "queries_per_step": B * L, "plant": wl.notes, "seed": hex(wl.seed),
                    "launches": "one uocr_sparse_decode_step per step" if one_launch else
-                               f"per layer, {ns} micro-batch streams" + (", HIP graph" if args.graph else "")},
+                               f"per layer, {args.streams} micro-batch streams" + (", HIP graph" if args.graph else "")},
         "tokens_per_s": B / (ms_step * 1e-3),
         "step_hbm_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -690,16 +871,40 @@ def main():
                               "algorithmic_bytes_per_launch": idx_bytes,
                               "traffic": traffic_for("indexer_decode")}
 
+    if not args.no_schedules:
+        # the same step under each schedule (the headline's included, for a
+        # like-for-like comparison in one place)
+        result["step_schedules"] = schedule_timings(U, torch, dev, cfg, (scores, idx, out, lse), step_ws_sched,
+                                                    args.steps, args.warmup, step_bytes)
+        log("step schedules: " + ", ".join(f"{k} {v['us_per_step']:.1f} us ({v['hbm_frac']:.3f} of HBM peak)"
+                                           for k, v in result["step_schedules"].items()))
+
     if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle on {16 * args.cpu_layers} query-layers")
-        nq, secs = cpu_baseline(dev, wl, args.cpu_layers)
+        log(f"CPU oracle on {B * args.cpu_layers} query-layers (all BLAS threads, then one thread), "
+            f"checked against the timed step's outputs")
+        timing, parity = cpu_baseline(U, dev, wl, args.cpu_layers, gpu_out, cfg)
+        nq = timing["queries"]
+        host = host_description()
+        blas_threads = max([d["threads"] or 1 for d in host["blas"]] or [1])
         result["cpu_baseline"] = {
-            "value": nq * H / secs, "unit": "query-heads/s", "cores": 1, "kind": "oracle",
-            "sample": f"{nq} oracle decode queries: {16 * args.cpu_layers} query-layers ({args.cpu_layers} layers "
-                      f"x 16 sequences) of the same workload, each computed twice; oracle time only (inputs "
-                      f"copied from device memory beforehand), {secs:.1f} s on 1 thread",
+            "value": nq * H / timing["seconds_all_threads"], "unit": "query-heads/s", "cores": blas_threads,
+            "kind": "oracle",
+            "sample": f"every query of the step: {nq} decode queries ({args.cpu_layers} layers x {B} sequences) of "
+                      f"the same workload on the same device inputs copied to the host, "
+                      f"{timing['seconds_all_threads']:.1f} s with numpy's BLAS on {blas_threads} threads (the "
+                      f"dot products; the block max, sort and softmax are single-threaded); oracle time only",
+            "single_thread": {"value": nq * H / timing["seconds_one_thread"], "cores": 1,
+                              "seconds": timing["seconds_one_thread"]},
+            "host": host,
         }
-        log(f"cpu oracle {nq * H / secs:.1f} query-heads/s")
+        result["parity"] = dict(parity, what="the timed step's selections and attention outputs against the CPU "
+                                              "oracle on the same inputs, every query")
+        log(f"cpu oracle {nq * H / timing['seconds_all_threads']:.1f} query-heads/s on {blas_threads} BLAS threads, "
+            f"{nq * H / timing['seconds_one_thread']:.1f} on one; parity: {parity['selection_exact']} exact, "
+            f"{parity['selection_differences_inside_band']} inside the band, "
+            f"{parity['selection_mismatches_outside_band']} outside; attention max-abs "
+            f"{parity['attention_on_gpu_selection']['max_abs']:.2e} rel-L2 "
+            f"{parity['attention_on_gpu_selection']['rel_l2']:.2e}; pass={parity['pass']}")
 
     if not args.no_dense:
         # Dense full-context attention of the same step (the comparator for the
@@ -727,7 +932,7 @@ def main():
         log(f"dense full-context attention step {ms_dense:.2f} ms ({dense_bytes / (ms_dense * 1e-3) / 1e9:.0f} GB/s): "
             f"sparse step is {ms_dense / ms_step:.1f}x faster")
         del dws
-    del dev, kvs, groups
+    del dev, kvs
     torch.cuda.empty_cache()
     if one_launch and not args.no_layout:
         # The same step with every sequence's blocks in consecutive pool slots
@@ -781,9 +986,7 @@ def main():
     if not args.no_short:
         result["short_context"] = run_short_contexts(U, SD, W, torch)
         for k, v in result["short_context"].items():
-            u = v["us_per_step"]
-            log(f"{k}: per-layer launches {u['per_layer']:.1f} us, one launch {u['one_launch']:.1f} us, "
-                f"automatic {u['auto']:.1f} us per step")
+            log(f"{k}: " + ", ".join(f"{n} {u:.1f} us" for n, u in v["us_per_step"].items()) + " per step")
 
     if not args.no_rope:
         result["page2d_rope_cache_write"] = run_rope(U, torch)
@@ -796,6 +999,9 @@ def main():
             f"{v['no_eviction_GB']:.2f} GB without eviction")
 
     print(json.dumps(result), flush=True)
+    if "parity" in result and not result["parity"]["pass"]:
+        log("PARITY FAILURE: " + "; ".join(result["parity"]["failures"]))
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -22,7 +22,7 @@ __all__ = [
     "workspace_size", "status_string", "last_error", "abi_version",
     "OP_INDEXER_DECODE", "OP_TOPK_DECODE", "OP_ATTN_DECODE",
     "OP_INDEXER_PREFILL", "OP_TOPK_PREFILL", "OP_ATTN_PREFILL", "OP_DENSE_ATTN_DECODE", "dense_attn_decode",
-    "OP_DECODE_STEP", "sparse_decode_step", "STEP_AUTO", "STEP_ONE_LAUNCH", "STEP_PER_LAYER",
+    "OP_DECODE_STEP", "sparse_decode_step", "check_decode_step", "DecodeStepWaitError", "STEP_AUTO", "STEP_ONE_LAUNCH", "STEP_PER_LAYER",
     "rope_cache_write", "rope_queries", "page_coords", "BlockPool", "PageWindow",
 ]
 
@@ -109,7 +109,7 @@ _SIGS = {
     "uocr_pool_table": ([_P, _I32, _P, _I32, _P], ctypes.c_int),
     "uocr_pool_used": ([_P], ctypes.c_int64),
     "uocr_pool_peak": ([_P], ctypes.c_int64),
-    "uocr_page_window_run": ([ctypes.POINTER(PageWindow), _P, _P, _I32, _P, _I32, _P, _I32], ctypes.c_int),
+    "uocr_page_window_run": ([ctypes.POINTER(PageWindow), _P, _P, _I32, _P, _I32, _P, _I32, _P], ctypes.c_int),
     "uocr_workspace_size": ([_CFG, _I32, _I32, _I32], ctypes.c_size_t),
     "uocr_status_string": ([_I32], ctypes.c_char_p),
     "uocr_last_error": ([], ctypes.c_char_p),
@@ -206,14 +206,41 @@ def dense_attn_decode(cfg: SparseCfg, kv: KV, q, out, lse=None, ws=None, stream=
 
 
 def sparse_decode_step(cfg: SparseCfg, kv: KV, n_layers: int, q_idx, q, block_scores, block_idx, out, lse=None,
-                       n_sel=None, ws=None, stream=None, schedule: int = 0) -> None:
+                       n_sel=None, ws=None, stream=None, schedule: int = 0, check: bool = False) -> None:
     """Scoring, selection and attention of every layer of a batch;
     ``kv`` describes layer 0 of layer-major pools.  ``schedule``:
-    STEP_AUTO, STEP_ONE_LAUNCH or STEP_PER_LAYER."""
+    STEP_AUTO, STEP_ONE_LAUNCH or STEP_PER_LAYER.  ``check=True`` (``ws`` a
+    tensor) waits for the call on its stream and raises
+    ``DecodeStepWaitError`` if a dependency wait of the one launch gave up
+    (the workspace's error word; the results are then undefined)."""
     _check(_lib.uocr_sparse_decode_step(ctypes.byref(cfg), ctypes.byref(kv), int(n_layers), int(schedule),
                                         _ptr(q_idx), _ptr(q),
                                         _ptr(block_scores), _ptr(block_idx), _ptr(n_sel), _ptr(out), _ptr(lse),
                                         _ptr(ws), _nbytes(ws), _stream(stream)), "sparse_decode_step")
+    if check:
+        check_decode_step(ws, stream)
+
+
+class DecodeStepWaitError(RuntimeError):
+    """A dependency wait of the one-launch decode step gave up."""
+
+
+def check_decode_step(ws, stream=None) -> None:
+    """Wait for the work queued on ``stream`` and read the error word (the
+    second 32-bit word) of a decode-step workspace tensor; raise
+    ``DecodeStepWaitError`` when it is nonzero.  Each one-launch call clears
+    it first, so it reports the last such call on this workspace."""
+    import torch
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("check_decode_step reads the workspace: pass it as a tensor")
+    if stream is None or isinstance(stream, int):
+        torch.cuda.current_stream().synchronize() if stream is None else torch.cuda.synchronize()
+    else:
+        stream.synchronize()
+    word = int(ws.view(torch.uint8)[4:8].cpu().view(torch.int32)[0])
+    if word != 0:
+        raise DecodeStepWaitError(f"a dependency wait of the one-launch decode step gave up (error word {word:#x}); "
+                                  "its results are undefined")
 
 
 def rope_cache_write(cfg: SparseCfg, kv: KV, n: int, seq, pos, tok_pos, page_pos, k_new, v_new, kidx_new,
@@ -306,12 +333,12 @@ class BlockPool:
             raise ValueError("image_tokens and text_tokens need one entry per page")
         img = (ctypes.c_int32 * max(n, 1))(*[int(v) for v in image_tokens])
         txt = (ctypes.c_int32 * max(n, 1))(*[int(v) for v in text_tokens])
-        peaks = (ctypes.c_int64 * max(n, 1))()
+        peaks = (ctypes.c_int64 * max(n, 1))()  # a document has at most one window per page
+        n_windows = ctypes.c_int32(0)
         cfg = PageWindow(int(window_pages), int(text_tail_tokens))
-        _check(_lib.uocr_page_window_run(ctypes.byref(cfg), img, txt, n, self._h, int(seq), peaks, n),
-               "page_window_run")
-        n_windows = n if n <= 1 else 1 + (n - 2) // (int(window_pages) - 1)
-        return [int(v) for v in peaks[:n_windows]]
+        _check(_lib.uocr_page_window_run(ctypes.byref(cfg), img, txt, n, self._h, int(seq), peaks, n,
+                                         ctypes.byref(n_windows)), "page_window_run")
+        return [int(v) for v in peaks[:n_windows.value]]
 
 
 def workspace_size(cfg: SparseCfg, op: int, rows: int, max_blocks: int) -> int:

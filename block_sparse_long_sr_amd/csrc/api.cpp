@@ -415,6 +415,9 @@ int uocr_indexer_score_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, co
   if (cand_ws_bytes < plan.ws_bytes)
     return fail(UOCR_EWORKSPACE, "cand_ws has %zu bytes, %zu needed", cand_ws_bytes, plan.ws_bytes);
   TRY(check_page_gate(kv));
+  if (kv->block_page != nullptr && kv->max_blocks > uocr::kMaxBlocksPrefillTiered)
+    return fail(UOCR_EUNSUPPORTED, "page-tiered prefill scoring supports max_blocks <= %d (got %d)",
+                uocr::kMaxBlocksPrefillTiered, kv->max_blocks);
   uocr::IndexerPrefillArgs a{};
   a.kidx_pool = kv->kidx_pool;
   a.block_table = kv->block_table;

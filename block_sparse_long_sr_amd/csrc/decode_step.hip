@@ -31,8 +31,6 @@
 // acquire fence (an L1/L2 invalidation of its XCD) before reading, so it
 // cannot hit a stale line.  No L2 write-back is needed on the writer's side.
 // A clear kernel zeroes the counters before each launch.
-#include <atomic>
-
 #include "attn_common.h"
 #include "device_common.h"
 #include "indexer_common.h"
@@ -244,27 +242,27 @@ DecodeStepPlan decode_step_plan(int32_t n_layers, int32_t batch, int32_t heads, 
 }
 
 namespace {
+// Workgroups of the step kernel that fit on one compute unit: its launch
+// bounds allow 128 VGPRs per lane at 4 waves per SIMD, i.e. two 8-wave
+// workgroups, and its LDS (well under half of the 160 KB of a CU) does not
+// lower that.
+constexpr int kStepGroupsPerCu = 2;
+static_assert(sizeof(SelectSmem<kStepThreads>) + sizeof(AttendSmem<kStepThreads>) + 4 * kMaxFusedTopk +
+                      4 * kMaxStepChunk + 64 <=
+                  160 * 1024 / kStepGroupsPerCu,
+              "two step workgroups must fit in one CU's LDS");
+
 template <int KPT>
 hipError_t launch_step(const DecodeStepArgs& a, int64_t items, hipStream_t stream) {
-  // One resident wave of workgroups (they loop over the tickets); a grid
-  // larger than what fits is also correct, the extra groups find no ticket.
-  // The count is computed once per device (threads that race here store
-  // the same value).
-  static std::atomic<int> resident[64];
-  int dev = 0;
+  // One resident wave of workgroups (they loop over the tickets).  A grid
+  // larger than what fits is also correct: a workgroup takes a ticket only
+  // once it runs, so late ones find none left.
+  int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  int fit = resident[dev].load(std::memory_order_relaxed);
-  if (fit == 0) {
-    int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_step_kernel<KPT>, kStepThreads, 0);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    fit = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
-    resident[dev].store(fit, std::memory_order_relaxed);
-  }
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t fit = (int64_t)kStepGroupsPerCu * (cus > 0 ? cus : 1);
   const int64_t grid = items < fit ? items : fit;
   hipLaunchKernelGGL(decode_step_kernel<KPT>, dim3((unsigned)grid), dim3(kStepThreads), 0, stream, a);
   return hipGetLastError();

@@ -30,7 +30,8 @@
 // A list entry packs the block score's 32-bit order key with its low idbits
 // replaced by the (complemented) in-split block index.  Ranking therefore
 // uses scores truncated to 2^-(23 - idbits) relative (2^-17 at 128K
-// context), equal truncated scores going to the lower block id.  Entries are
+// context, one bit less with the page tier in the top bit), equal truncated
+// scores going to the lower block id.  Entries are
 // unique, so a sorted insertion is one median of three per slot.
 //
 // The 128-dim contraction is split into 8 MFMA steps of 16; lane half h of an
@@ -356,9 +357,13 @@ PrefillPlan prefill_plan(int32_t T, int32_t max_blocks, int32_t topk, int32_t lo
   }
   // About one workgroup per compute unit (more for long chunks), 16 to
   // kMaxBps blocks per split, at most 64 splits (max_blocks <= 64 * kMaxBps).
+  // Up to 64 * 256 blocks a split holds at most 256 blocks, so in-split ids
+  // take at most 8 bits (ranking to 2^-15 relative, 2^-14 with page tiers);
+  // only longer contexts need 9 (2^-14, plain ranking only).
   int64_t bps = ((int64_t)max_blocks * p.n_tiles + 255) / 256;
   if (bps < 16) bps = 16;
   if (bps > kMaxBps) bps = kMaxBps;
+  if (max_blocks <= kMaxBlocksPrefillTiered && bps > kMaxBps / 2) bps = kMaxBps / 2;
   const int64_t min_bps = ((int64_t)max_blocks + 63) / 64;
   if (bps < min_bps) bps = min_bps;
   p.bps = (int32_t)bps;

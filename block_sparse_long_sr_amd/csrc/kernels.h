@@ -247,5 +247,9 @@ hipError_t launch_topk_prefill(const TopkPrefillArgs& a, hipStream_t stream);
 // Largest in-split index width: packed prefill keys keep 32 - idbits order
 // bits, i.e. scores are ranked to 2^-(23 - idbits) relative.
 constexpr int32_t kMaxIdBits = 9;
+// Longest context (in blocks) of a page-tiered prefill scoring: up to here
+// splits hold at most 256 blocks (idbits <= 8), so with the tier bit a score
+// still ranks to 2^-14 relative, inside the 1e-4 band of selection parity.
+constexpr int32_t kMaxBlocksPrefillTiered = 64 * 256;
 
 }  // namespace uocr

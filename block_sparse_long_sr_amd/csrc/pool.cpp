@@ -168,7 +168,8 @@ int64_t uocr_pool_used(const uocr_pool* pool) { return pool == nullptr ? -1 : po
 int64_t uocr_pool_peak(const uocr_pool* pool) { return pool == nullptr ? -1 : pool->peak; }
 
 int uocr_page_window_run(const uocr_page_window* cfg, const int32_t* image_tokens, const int32_t* text_tokens,
-                         int32_t n_pages, uocr_pool* pool, int32_t seq, int64_t* window_peaks, int32_t max_windows) {
+                         int32_t n_pages, uocr_pool* pool, int32_t seq, int64_t* window_peaks, int32_t max_windows,
+                         int32_t* n_windows_out) {
   if (cfg == nullptr || image_tokens == nullptr || text_tokens == nullptr)
     return uocr::set_error(UOCR_EINVAL, "cfg, image_tokens and text_tokens must not be NULL");
   if (int st = check_seq(pool, seq)) return st;
@@ -182,6 +183,7 @@ int uocr_page_window_run(const uocr_page_window* cfg, const int32_t* image_token
   if (window_peaks != nullptr && max_windows < n_windows)
     return uocr::set_error(UOCR_ESHAPE, "window_peaks holds %d entries, the document has %d windows", max_windows,
                            n_windows);
+  if (n_windows_out != nullptr) *n_windows_out = n_windows;
   // Window w covers pages [w(W-1), w(W-1) + W); its first page (w > 0) is the
   // page shared with window w-1: image reused, text already produced.
   for (int32_t w = 0; w < n_windows; ++w) {

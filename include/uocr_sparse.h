@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define UOCR_ABI_VERSION 3
+#define UOCR_ABI_VERSION 4
 
 /* Status codes. */
 enum {
@@ -284,13 +284,15 @@ int uocr_dense_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const 
  *   cand_ws : workspace of uocr_workspace_size(cfg, UOCR_OP_INDEXER_PREFILL,
  *             T, max_blocks) bytes
  * Ranking precision: a list entry keeps a block score's order bits above an
- * in-split block index of idbits = ceil(log2(blocks per split)) <= 9 bits, so
- * rows are ranked on scores truncated to 2^-(23-idbits) relative (2^-17 at
- * 128K context, 2^-14 at worst; one bit less with page tiers), equal
- * truncated scores going to the lower block id.
+ * in-split block index of idbits = ceil(log2(blocks per split)) bits, so rows
+ * are ranked on scores truncated to 2^-(23-idbits) relative, equal truncated
+ * scores going to the lower block id.  Up to 16384 blocks a split holds at
+ * most 256 blocks (idbits <= 8: 2^-17 at 128K context, 2^-15 at worst);
+ * longer contexts take 9 bits (2^-14).  Page tiers take one more bit.
  * Requires 0 <= q_start, T >= 0, q_start + T <= 32 * max_blocks <= 32 * 32768,
- * topk_blocks - local_blocks <= 16 (UOCR_EUNSUPPORTED beyond).  With page
- * tags, kv->query_page holds one page per row ([T]).
+ * topk_blocks - local_blocks <= 16, and with page tags max_blocks <= 16384
+ * (UOCR_EUNSUPPORTED beyond; the tier bit then keeps scores ranked to 2^-14
+ * relative).  With page tags, kv->query_page holds one page per row ([T]).
  */
 int uocr_indexer_score_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q_idx,
                                int32_t q_start, int32_t T, void* cand_ws, size_t cand_ws_bytes, void* stream);
@@ -429,7 +431,9 @@ int64_t uocr_pool_peak(const uocr_pool* pool);
  * when w > 0), then their text; before the next window, uocr_pool_keep
  * keeps the visual tokens of the window's last page and its last
  * text_tail_tokens text tokens.  window_peaks[w] (if not NULL; max_windows
- * entries) gets the most blocks in use during window w.  Errors: UOCR_EINVAL
+ * entries) gets the most blocks in use during window w; *n_windows (if not
+ * NULL) the number of windows, 0 for no page and 1 + (n_pages - 2) / (W - 1)
+ * otherwise, written once the arguments have passed their checks.  Errors: UOCR_EINVAL
  * for NULL arguments, UOCR_ESHAPE for a bad config, a non-empty sequence,
  * negative page sizes or too small a window_peaks (all checked before any
  * change), UOCR_ECAPACITY when the pool runs out part-way (the sequence then
@@ -440,7 +444,8 @@ typedef struct uocr_page_window {
   int32_t text_tail_tokens;
 } uocr_page_window;
 int uocr_page_window_run(const uocr_page_window* cfg, const int32_t* image_tokens, const int32_t* text_tokens,
-                         int32_t n_pages, uocr_pool* pool, int32_t seq, int64_t* window_peaks, int32_t max_windows);
+                         int32_t n_pages, uocr_pool* pool, int32_t seq, int64_t* window_peaks, int32_t max_windows,
+                         int32_t* n_windows);
 
 /* ------------------------------------------------------------- utilities */
 

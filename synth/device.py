@@ -78,6 +78,51 @@ class DeviceWorkload:
         return U.make_kv(self.k[li], self.v[li], self.kidx[li], self.block_table, self.ctx_lens,
                          self.wl.pool_blocks, self.wl.batch, self.wl.max_blocks)
 
+    # ---- host copies of the device inputs, in logical order ---------------
+    # The oracle side of a full-size parity check takes its inputs from here:
+    # the very bits the kernels read, gathered through the block table and
+    # copied to the host (the 135 GB workloads are not regenerated on the
+    # host).  Only generated inputs are read, never a kernel's output.
+
+    def host_kidx(self, li: int, seq: int, n_tokens: int) -> np.ndarray:
+        """Indexer keys of tokens [0, n_tokens) of sequence ``seq`` in resident
+        layer ``li``: [n_tokens, Di] uint16."""
+        nb = -(-int(n_tokens) // W.BLOCK)
+        if nb == 0:
+            return np.zeros((0, self.wl.index_dim), np.uint16)
+        blocks = self.block_table[seq, :nb].long()
+        rows = self.kidx[li].index_select(0, blocks).reshape(nb * W.BLOCK, -1)[:n_tokens]
+        return rows.cpu().numpy().view(np.uint16)
+
+    def host_kv_fetch(self, li: int, seq: int):
+        """``fetch(tokens) -> (K, V)``, each [H, len(tokens), D] uint16: the main
+        keys and values of the given token positions of ``seq`` in layer ``li``."""
+        import torch
+
+        tab = self.block_table
+        dev = tab.device
+
+        def fetch(toks):
+            toks = np.asarray(toks, np.int64)
+            t = torch.from_numpy(toks).to(dev)
+            pb = tab[seq, t // W.BLOCK].long()
+            off = t % W.BLOCK
+            n = torch.arange(toks.size, device=dev)
+            k = self.k[li].index_select(0, pb)[n, :, off, :]
+            v = self.v[li].index_select(0, pb)[n, :, off, :]
+            return (k.transpose(0, 1).contiguous().cpu().numpy().view(np.uint16),
+                    v.transpose(0, 1).contiguous().cpu().numpy().view(np.uint16))
+
+        return fetch
+
+    def host_decode_queries(self, li: int, seq: int):
+        """(q [H, D], q_idx [Di]) uint16 of a decode query."""
+        return (self.q[li, seq].cpu().numpy().view(np.uint16), self.q_idx[li, seq].cpu().numpy().view(np.uint16))
+
+    def host_prefill_queries(self):
+        """(q [T, H, D], q_idx [T, Di]) uint16 of a prefill chunk."""
+        return self.q.cpu().numpy().view(np.uint16), self.q_idx.cpu().numpy().view(np.uint16)
+
 
 def _alloc(wl: W.Workload, layers: List[int], device):
     import torch

@@ -76,16 +76,19 @@ def gpu_attn_decode(dev, li: int, cfg, idx_np: np.ndarray):
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
-def gpu_prefill(dev, cfg, idx_override: Optional[np.ndarray] = None, block_major: bool = True) -> Dict[str, np.ndarray]:
+def gpu_prefill(dev, cfg, idx_override: Optional[np.ndarray] = None, block_major: bool = True,
+                fill=(0xA5, 0x5A)) -> Dict[str, np.ndarray]:
     """Scoring, merge and attention of a prefill chunk; the attention runs
-    block-major (with its workspace) unless block_major is False."""
+    block-major (with its workspace) unless block_major is False.  The
+    scoring and attention workspaces start filled with the bytes ``fill``
+    (stale contents must not matter)."""
     wl = dev.wl
     T, M, H, D = wl.rows, wl.max_blocks, wl.heads, wl.head_dim
     topk = cfg.topk_blocks
     kv = dev.kv(0)
     ws_bytes = U.workspace_size(cfg, U.OP_INDEXER_PREFILL, T, M)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-    ws.fill_(0xA5)
+    ws.fill_(fill[0])
     idx = torch.full((T, topk), -7, dtype=torch.int32, device="cuda")
     nsel = torch.full((T,), -7, dtype=torch.int32, device="cuda")
     out = torch.full((T, H, D), float("nan"), dtype=torch.float32, device="cuda")
@@ -99,7 +102,7 @@ def gpu_prefill(dev, cfg, idx_override: Optional[np.ndarray] = None, block_major
         ab = U.workspace_size(cfg, U.OP_ATTN_PREFILL, T, M)
         assert ab > 0
         aws = torch.empty(ab, dtype=torch.uint8, device="cuda")
-        aws.fill_(0x5A)  # stale contents must not matter
+        aws.fill_(fill[1])
     U.sparse_attn_prefill(cfg, kv, dev.q, wl.q_start, T, idx_in, out, lse, ws=aws)
     torch.cuda.synchronize()
     return {"idx": idx.cpu().numpy(), "nsel": nsel.cpu().numpy(), "out": out.cpu().numpy(),
@@ -227,3 +230,93 @@ def full_decode_check(dev, wl: W.Workload, li: int, layer: int, seqs, cfg_u, cfg
             o2, l2 = oracle_attend_with(wl, layer, b, wl.q(layer, b), got, L - 1, cfg_o)
             check_attention(res["out"][b], res["lse"][b], o2, l2)
     return stats
+
+
+# ------------------------------------------- full-size checks (D2H inputs)
+# At the measured sizes the oracle takes the device inputs themselves, copied
+# to the host (DeviceWorkload.host_*), instead of regenerating 135 GB of
+# caches on the host; the device generator is pinned to the host generator
+# bit for bit in test_synth / test_gpu_decode.
+
+def oracle_decode_d2h(dev, li: int, b: int, cfg_o, block_page=None, query_page=None):
+    """Oracle result of decode query (resident layer li, sequence b) on the
+    device inputs; returns (ref, q, q_idx, kidx, fetch)."""
+    L = int(dev.wl.ctx_lens[b])
+    kidx = dev.host_kidx(li, b, L)
+    q, qi = dev.host_decode_queries(li, b)
+    fetch = dev.host_kv_fetch(li, b)
+    ref = oracle.decode_query_fetch(q, qi, kidx, fetch, L, cfg_o, block_page, query_page)
+    return ref, q, qi, kidx, fetch
+
+
+def check_query_end_to_end(ref, q, fetch, p: int, cfg_o, idx_row, out, lse):
+    """Selection under the band rule, then the GPU's attention output against
+    the oracle's on the GPU's own set (the oracle's when they are equal)."""
+    check_selection(idx_row, ref, cfg_o.topk_blocks)
+    got = [int(x) for x in idx_row if x >= 0]
+    if got == ref["selected"]:
+        return check_attention(out, lse, ref["out"], ref["lse"]), got != ref["selected"]
+    toks = oracle.attended_tokens(got, p, cfg_o)
+    k, v = fetch(toks)
+    o2, l2 = oracle.attend(q, k, v, np.arange(toks.size), cfg_o.sm_scale)
+    return check_attention(out, lse, o2, l2), True
+
+
+def check_decode_full(dev, res, queries, cfg_u, cfg_o, tags=None, qpages=None, scores=True):
+    """Every (resident layer, sequence) in ``queries`` against the oracle on
+    the device inputs: block scores (within the summation-order bound),
+    selection (band rule), the GPU's attention on the GPU's selection and,
+    per layer, the GPU's attention on the oracle's own index set.
+    ``res``: host arrays idx [nl][B][topk], out [nl][B][H][D], lse
+    [nl][B][H] and (with scores) scores [nl][B][M].  Returns a summary."""
+    wl = dev.wl
+    topk = cfg_u.topk_blocks
+    by_layer: Dict[int, Dict[int, Dict]] = {}
+    band_diffs = 0
+    worst = [0.0, 0.0]
+    for li, b in queries:
+        bp = None if tags is None else tags[b]
+        qp = None if qpages is None else int(qpages[b])
+        ref, q, qi, kidx, fetch = oracle_decode_d2h(dev, li, b, cfg_o, bp, qp)
+        L = int(wl.ctx_lens[b])
+        if scores and L > 0:
+            check_scores(res["scores"][li][b], ref, qi, kidx, wl.max_blocks)
+        (err, rel), differs = check_query_end_to_end(ref, q, fetch, L - 1, cfg_o, res["idx"][li][b],
+                                                     res["out"][li][b], res["lse"][li][b])
+        band_diffs += int(differs)
+        worst = [max(worst[0], err), max(worst[1], rel)]
+        by_layer.setdefault(li, {})[b] = ref
+    # the attention itself, measured with the oracle's index set
+    for li, refs in by_layer.items():
+        idx_o = np.full((wl.batch, topk), -1, np.int32)
+        for b, ref in refs.items():
+            idx_o[b] = pad_idx(ref["selected"], topk)
+        out_o, lse_o = gpu_attn_decode(dev, li, cfg_u, idx_o)
+        for b, ref in refs.items():
+            err, rel = check_attention(out_o[b], lse_o[b], ref["out"], ref["lse"])
+            worst = [max(worst[0], err), max(worst[1], rel)]
+    return {"queries": len(queries), "band_differences": band_diffs, "max_abs": worst[0], "rel_l2": worst[1]}
+
+
+def gpu_decode_step(dev, cfg, schedule, tags=None, qpages=None) -> Dict[str, np.ndarray]:
+    """uocr_sparse_decode_step over every resident layer of dev (layer-major
+    outputs, host copies); ``err`` is the workspace's error word after a
+    one-launch call (the other schedules leave the workspace alone)."""
+    wl = dev.wl
+    nl, B, M, H, D = dev.q.shape[0], wl.batch, wl.max_blocks, wl.heads, wl.head_dim
+    topk = cfg.topk_blocks
+    bp = None if tags is None else torch.from_numpy(np.ascontiguousarray(tags, dtype=np.int32)).cuda()
+    qp = None if qpages is None else torch.from_numpy(np.ascontiguousarray(qpages, dtype=np.int32)).cuda()
+    kv = U.make_kv(dev.k[0], dev.v[0], dev.kidx[0], dev.block_table, dev.ctx_lens, wl.pool_blocks, B, M, bp, qp)
+    scores = torch.full((nl, B, M), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((nl, B, topk), -7, dtype=torch.int32, device="cuda")
+    nsel = torch.full((nl, B), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((nl, B, H, D), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((nl, B, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(U.workspace_size(cfg, U.OP_DECODE_STEP, nl * B, M), dtype=torch.uint8, device="cuda")
+    U.sparse_decode_step(cfg, kv, nl, dev.q_idx, dev.q, scores, idx, out, lse, n_sel=nsel, ws=ws,
+                         schedule=schedule)
+    torch.cuda.synchronize()
+    return {"scores": scores.cpu().numpy(), "idx": idx.cpu().numpy(), "nsel": nsel.cpu().numpy(),
+            "out": out.cpu().numpy(), "lse": lse.cpu().numpy(),
+            "err": int(ws[4:8].cpu().numpy().view(np.uint32)[0])}

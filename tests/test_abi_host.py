@@ -77,7 +77,7 @@ def test_struct_layouts_match_header(U, tmp_path):
         assert int(got[st]) == ctypes.sizeof(cls)
         for f in fields[st]:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, f
-    assert int(got["abi"]) == U.abi_version() == 3
+    assert int(got["abi"]) == U.abi_version() == 4
 
 
 def test_status_strings(U):
@@ -254,6 +254,27 @@ def test_page_tags_need_query_pages(U):
     with pytest.raises(U.UocrError) as e:
         U.indexer_score_prefill(cfg, kv1, FAKE, 1900, 100, (FAKE, ws), stream=0)
     assert e.value.status == 1 and "block_page" in U.last_error()
+
+
+def test_page_tiered_prefill_context_limit(U):
+    """With page tags a prefill ranking key spends one bit on the tier; up to
+    16384 blocks the in-split ids take at most 8 bits, so scores still rank
+    to 2^-14 relative (inside the 1e-4 band).  Longer tiered contexts (9-bit
+    ids) are rejected; plain ranking still takes them."""
+    cfg = U.make_cfg()
+    for M, status in ((16385, 5), (32768, 5)):
+        kv = _kv(U, batch=1, max_blocks=M)
+        kv.block_page, kv.query_page = FAKE, FAKE
+        with pytest.raises(U.UocrError) as e:
+            U.indexer_score_prefill(cfg, kv, FAKE, 0, 100, (FAKE, 1 << 30), stream=0)
+        assert e.value.status == status and "16384" in U.last_error()
+    # 16384 blocks with tags passes every check (the launch itself is not
+    # reached here: a bad workspace size stops it first)
+    kv = _kv(U, batch=1, max_blocks=16384)
+    kv.block_page, kv.query_page = FAKE, FAKE
+    with pytest.raises(U.UocrError) as e:
+        U.indexer_score_prefill(cfg, kv, FAKE, 0, 100, (FAKE, 16), stream=0)
+    assert e.value.status == 3
 
 
 def test_empty_batch_is_a_no_op(U):

@@ -191,3 +191,30 @@ def test_page_gate_prefill_rows_on_two_pages(values):
         else:
             o2, l2 = G.oracle_attend_with(wl, 0, 0, q[t], got, wl.q_start + t, cfg_o)
             G.check_attention(res["out"][t], res["lse"][t], o2, l2)
+
+
+def test_page_gate_prefill_long_chunk_8bit_split_ids():
+    """A 8704-row chunk at 128K with page tags: 17 row tiles would ask for
+    splits of 272 blocks (9-bit in-split ids); the plan holds splits to 256
+    blocks (8-bit ids), so with the tier bit a score still ranks to 2^-14
+    relative, inside the 1e-4 band.  Sampled rows on every row tile against
+    the oracle on the device inputs."""
+    S, T = 131072, 8704
+    wl = W.prefill_case("page gate prefill T=8704 at 122368 of 131072", 0xD5, S, S - T, T)
+    print("case:", wl.name, flush=True)
+    cfg_u, cfg_o = G.cfg_for(wl), G.ocfg()
+    M = wl.max_blocks
+    assert U.workspace_size(cfg_u, U.OP_INDEXER_PREFILL, T, M) == T * (M // 256) * 12 * 4
+    dev = SD.generate(wl)
+    tags = W.page_tags(M)
+    row_pages = np.array([W.page_of(wl.q_start + t) for t in range(T)], np.int32)
+    res = gated_prefill(dev, cfg_u, tags, row_pages)
+    kidx = dev.host_kidx(0, 0, S)
+    q, qi = dev.host_prefill_queries()
+    fetch = dev.host_kv_fetch(0, 0)
+    rows = sorted(set([0, 1, 31, 511, 512, 4095, 4096, 8191, 8192, T - 1] + list(range(7, T, 613))))
+    refs = oracle.prefill_rows_fetch(q, qi, kidx, fetch, wl.q_start, rows, cfg_o, tags, row_pages)
+    for r in refs:
+        t = r["row"]
+        assert res["nsel"][t] == min(16, (wl.q_start + t) // 32 + 1)
+        G.check_query_end_to_end(r, q[t], fetch, wl.q_start + t, cfg_o, res["idx"][t], res["out"][t], res["lse"][t])
