@@ -22,7 +22,7 @@ __all__ = [
     "workspace_size", "status_string", "last_error", "abi_version",
     "OP_INDEXER_DECODE", "OP_TOPK_DECODE", "OP_ATTN_DECODE",
     "OP_INDEXER_PREFILL", "OP_TOPK_PREFILL", "OP_ATTN_PREFILL", "OP_DENSE_ATTN_DECODE", "dense_attn_decode",
-    "OP_DECODE_STEP", "sparse_decode_step", "check_decode_step", "DecodeStepWaitError", "STEP_AUTO", "STEP_ONE_LAUNCH", "STEP_PER_LAYER",
+    "OP_DECODE_STEP", "sparse_decode_step", "sparse_decode_step_static", "check_decode_step", "DecodeStepWaitError", "STEP_AUTO", "STEP_ONE_LAUNCH", "STEP_PER_LAYER",
     "rope_cache_write", "rope_queries", "page_coords", "BlockPool", "PageWindow",
 ]
 
@@ -96,6 +96,7 @@ _SIGS = {
     "uocr_topk_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "uocr_dense_attn_decode": ([_CFG, _KV, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "uocr_sparse_decode_step": ([_CFG, _KV, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "uocr_sparse_decode_step_static": ([_CFG, _KV, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "uocr_rope_cache_write": ([_CFG, _KV, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "uocr_rope_queries": ([_CFG, ctypes.c_int32, _P, _P, _P, _P, _P], ctypes.c_int),
     "uocr_indexer_score_prefill": ([_CFG, _KV, _P, _I32, _I32, _P, _SZ, _P], ctypes.c_int),
@@ -219,6 +220,18 @@ def sparse_decode_step(cfg: SparseCfg, kv: KV, n_layers: int, q_idx, q, block_sc
                                         _ptr(ws), _nbytes(ws), _stream(stream)), "sparse_decode_step")
     if check:
         check_decode_step(ws, stream)
+
+
+def sparse_decode_step_static(cfg: SparseCfg, kv: KV, n_layers: int, q_idx, q, block_scores, block_idx, out,
+                              lse=None, n_sel=None, status=None, stream=None, schedule: int = 0) -> None:
+    """``sparse_decode_step`` without a workspace (no allocation anywhere):
+    the one launch keeps its counters in the library's static device array.
+    ``status`` (int32 device tensor of one element, optional) gets 0, or 1
+    if a dependency wait gave up.  Calls that overlap on one GPU race."""
+    _check(_lib.uocr_sparse_decode_step_static(ctypes.byref(cfg), ctypes.byref(kv), int(n_layers), int(schedule),
+                                               _ptr(q_idx), _ptr(q), _ptr(block_scores), _ptr(block_idx),
+                                               _ptr(n_sel), _ptr(out), _ptr(lse), _ptr(status), _stream(stream)),
+           "sparse_decode_step_static")
 
 
 class DecodeStepWaitError(RuntimeError):

@@ -301,10 +301,17 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
   return hip_status(uocr::launch_select_attn(sa, static_cast<hipStream_t>(stream)), "topk_attn_decode");
 }
 
-int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n_layers, int32_t schedule,
-                            const uint16_t* q_idx,
-                            const uint16_t* q, float* block_scores, int32_t* block_idx, int32_t* n_sel, float* out,
-                            float* lse, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the two decode-step entry points.  counters: the caller's
+// workspace (ws, ws_bytes) or, with use_static, the library's static scratch
+// array, whose address is looked up only after every argument check passed.
+int decode_step_common(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n_layers, int32_t schedule,
+                       const uint16_t* q_idx, const uint16_t* q, float* block_scores, int32_t* block_idx,
+                       int32_t* n_sel, float* out, float* lse, void* ws, size_t ws_bytes, bool use_static,
+                       int32_t* status, void* stream, const char* name) {
   TRY(check_cfg(cfg));
   TRY(check_kv(kv, true, true));
   if (n_layers < 0) return fail(UOCR_ESHAPE, "n_layers must be >= 0 (got %d)", n_layers);
@@ -330,11 +337,29 @@ int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32
   OPT_PTR4(n_sel, "n_sel");
   REQ_PTR4(out, "out");
   OPT_PTR4(lse, "lse");
+  OPT_PTR4(status, "status");
   TRY(check_page_gate(kv));
-  if (ws == nullptr) return fail(UOCR_EWORKSPACE, "ws is NULL (%zu bytes needed)", plan.ws_bytes);
-  if (ws_bytes < plan.ws_bytes)
-    return fail(UOCR_EWORKSPACE, "ws holds %zu bytes, %zu needed", ws_bytes, plan.ws_bytes);
-  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(UOCR_EINVAL, "ws is not 256-byte aligned");
+  const bool one_launch = schedule == UOCR_STEP_ONE_LAUNCH ||
+                          (schedule == UOCR_STEP_AUTO &&
+                           uocr::decode_step_one_launch(n_layers, kv->batch, kv->max_blocks));
+  uint32_t* counters = nullptr;
+  if (use_static) {
+    if (one_launch && plan.counter_words > uocr::kStaticStepWords)
+      return fail(UOCR_EUNSUPPORTED,
+                  "the one launch without a workspace supports n_layers * batch <= %lld (got %lld); pass a "
+                  "workspace to uocr_sparse_decode_step",
+                  (long long)((uocr::kStaticStepWords - 2) / 3), (long long)n_layers * kv->batch);
+    if (one_launch) {
+      const hipError_t e = uocr::decode_step_static_counters(&counters);
+      if (e != hipSuccess) return fail(UOCR_EHIP, "%s: scratch address: %s", name, hipGetErrorString(e));
+    }
+  } else {
+    if (ws == nullptr) return fail(UOCR_EWORKSPACE, "ws is NULL (%zu bytes needed)", plan.ws_bytes);
+    if (ws_bytes < plan.ws_bytes)
+      return fail(UOCR_EWORKSPACE, "ws holds %zu bytes, %zu needed", ws_bytes, plan.ws_bytes);
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(UOCR_EINVAL, "ws is not 256-byte aligned");
+    counters = static_cast<uint32_t*>(ws);
+  }
   uocr::DecodeStepArgs a{};
   a.k_pool = kv->k_pool;
   a.v_pool = kv->v_pool;
@@ -352,7 +377,8 @@ int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32
   a.out = out;
   a.lse = lse;
   a.n_sel = n_sel;
-  a.counters = static_cast<uint32_t*>(ws);
+  a.counters = counters;
+  a.status_out = status;
   a.num_blocks = kv->num_blocks;
   a.n_layers = n_layers;
   a.batch = kv->batch;
@@ -363,11 +389,27 @@ int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32
   a.lag = plan.lag;
   a.chunk = plan.chunk;
   a.scale_log2 = cfg->sm_scale * 1.44269504088896340736f;
-  const bool one_launch = schedule == UOCR_STEP_ONE_LAUNCH ||
-                          (schedule == UOCR_STEP_AUTO &&
-                           uocr::decode_step_one_launch(n_layers, kv->batch, kv->max_blocks));
-  return hip_status(uocr::launch_decode_step(a, plan, one_launch, static_cast<hipStream_t>(stream)),
-                    "sparse_decode_step");
+  return hip_status(uocr::launch_decode_step(a, plan, one_launch, static_cast<hipStream_t>(stream)), name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n_layers, int32_t schedule,
+                            const uint16_t* q_idx,
+                            const uint16_t* q, float* block_scores, int32_t* block_idx, int32_t* n_sel, float* out,
+                            float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return decode_step_common(cfg, kv, n_layers, schedule, q_idx, q, block_scores, block_idx, n_sel, out, lse, ws,
+                            ws_bytes, false, nullptr, stream, "sparse_decode_step");
+}
+
+int uocr_sparse_decode_step_static(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n_layers,
+                                   int32_t schedule, const uint16_t* q_idx, const uint16_t* q, float* block_scores,
+                                   int32_t* block_idx, int32_t* n_sel, float* out, float* lse, int32_t* status,
+                                   void* stream) {
+  return decode_step_common(cfg, kv, n_layers, schedule, q_idx, q, block_scores, block_idx, n_sel, out, lse,
+                            nullptr, 0, true, status, stream, "sparse_decode_step_static");
 }
 
 int uocr_dense_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q, float* out, float* lse,

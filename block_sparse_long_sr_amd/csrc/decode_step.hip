@@ -31,6 +31,8 @@
 // acquire fence (an L1/L2 invalidation of its XCD) before reading, so it
 // cannot hit a stale line.  No L2 write-back is needed on the writer's side.
 // A clear kernel zeroes the counters before each launch.
+#include <mutex>
+
 #include "attn_common.h"
 #include "device_common.h"
 #include "indexer_common.h"
@@ -72,7 +74,7 @@ __device__ __forceinline__ Item item_of(uint32_t t, int S, int C, int H, int D) 
 // Thread 0 only: poll *ctr (relaxed, device scope) until it reaches need,
 // then one acquire fence at device scope (a single cache invalidation, not
 // one per poll).
-__device__ __forceinline__ void wait_count(uint32_t* ctr, uint32_t need, uint32_t* err) {
+__device__ __forceinline__ void wait_count(uint32_t* ctr, uint32_t need, uint32_t* err, int32_t* status_out) {
   for (uint32_t it = 0; it < kSpinLimit; ++it) {
     if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -81,6 +83,7 @@ __device__ __forceinline__ void wait_count(uint32_t* ctr, uint32_t need, uint32_
     __builtin_amdgcn_s_sleep(2);
   }
   __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (status_out != nullptr) __hip_atomic_store(status_out, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
@@ -101,8 +104,10 @@ __device__ __forceinline__ uint32_t count_done(uint32_t* ctr) {
 }
 }  // namespace
 
-__global__ __launch_bounds__(kStepThreads) void decode_step_clear_kernel(uint32_t* counters, int n) {
+__global__ __launch_bounds__(kStepThreads) void decode_step_clear_kernel(uint32_t* counters, int n,
+                                                                         int32_t* status_out) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) counters[i] = 0u;
+  if (status_out != nullptr && threadIdx.x == 0) *status_out = 0;
 }
 
 template <int KPT>
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
 
     if (!it.attention) {
       if (l > 0) {
-        if (tid == 0) wait_count(attn_done + (it.slot - B), (uint32_t)H, err);
+        if (tid == 0) wait_count(attn_done + (it.slot - B), (uint32_t)H, err, a.status_out);
         __syncthreads();
       }
       const int j0 = it.idx * chunk;
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
         if (tid == 0) count_done(sel_done + it.slot);
       }
     } else {
-      if (tid == 0) wait_count(sel_done + it.slot, 1u, err);
+      if (tid == 0) wait_count(sel_done + it.slot, 1u, err, a.status_out);
       __syncthreads();
       for (int i = tid; i < a.topk; i += kStepThreads) s_blocks[i] = sel_out[i];
       __syncthreads();
@@ -269,6 +274,35 @@ hipError_t launch_step(const DecodeStepArgs& a, int64_t items, hipStream_t strea
 }
 }  // namespace
 
+// The counters of uocr_sparse_decode_step_static, for callers that cannot
+// allocate a workspace: a fixed device array, one copy per GPU, held until
+// the process ends.  In host code `scratch` only names the symbol; its
+// device address on the current GPU comes from hipGetSymbolAddress, looked up
+// once per device and kept below.
+static __device__ __align__(256) uint32_t scratch[kStaticStepWords];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+uint32_t* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_status[kMaxDevices];
+}  // namespace
+
+hipError_t decode_step_static_counters(uint32_t** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
+  });
+  if (g_scratch_status[dev] != hipSuccess) return g_scratch_status[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 bool decode_step_one_launch(int32_t n_layers, int32_t batch, int32_t max_blocks) {
   // The one launch overlaps one sequence's selection and attention with the
   // scoring of others, but a sequence's layers stay in order: each layer of
@@ -287,7 +321,14 @@ hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& pla
   const int B = a.batch, M = a.max_blocks, H = a.heads;
   if (!one_launch) {
     // per-layer launches of the scoring kernel and the fused selection +
-    // attention kernel, on the caller's stream
+    // attention kernel, on the caller's stream (no waits: a status word
+    // only needs its 0)
+    if (a.status_out != nullptr) {
+      hipLaunchKernelGGL(decode_step_clear_kernel, dim3(1), dim3(kStepThreads), 0, stream, a.counters, 0,
+                         a.status_out);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     for (int l = 0; l < a.n_layers; ++l) {
       IndexerDecodeArgs ia{};
       ia.kidx_pool = a.kidx_pool + (int64_t)l * a.kidx_layer_stride;
@@ -332,7 +373,7 @@ hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& pla
     return hipSuccess;
   }
   hipLaunchKernelGGL(decode_step_clear_kernel, dim3(1), dim3(kStepThreads), 0, stream, a.counters,
-                     (int)plan.counter_words);
+                     (int)plan.counter_words, a.status_out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t max_cand = (int64_t)a.max_blocks - a.local_blocks;

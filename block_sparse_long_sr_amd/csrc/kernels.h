@@ -111,6 +111,7 @@ struct DecodeStepArgs {
   float* lse;                  // or null
   int32_t* n_sel;              // or null
   uint32_t* counters;          // workspace: ticket, error word, per-slot completion counts
+  int32_t* status_out;         // or null: 0 at the start, 1 if a dependency wait gave up
   int64_t num_blocks;
   int32_t n_layers;
   int32_t batch;
@@ -125,7 +126,7 @@ struct DecodeStepArgs {
 struct DecodeStepPlan {
   int32_t lag;            // slots between a slot's scoring and its attention items
   int32_t chunk;          // blocks per scoring item
-  int64_t counter_words;  // 2 + 2 * n_layers * batch
+  int64_t counter_words;  // 2 + 3 * n_layers * batch
   int64_t items;          // work items of the launch
   size_t ws_bytes;
 };
@@ -135,6 +136,11 @@ DecodeStepPlan decode_step_plan(int32_t n_layers, int32_t batch, int32_t heads, 
 bool decode_step_one_launch(int32_t n_layers, int32_t batch, int32_t max_blocks);
 hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& plan, bool one_launch,
                               hipStream_t stream);
+// Counters of the no-workspace variant: a static device array of
+// kStaticStepWords words (ticket, error word, three per layer-sequence slot);
+// *ptr gets its address on the current device (looked up once per device).
+constexpr int64_t kStaticStepWords = 65536;  // 256 KiB per GPU
+hipError_t decode_step_static_counters(uint32_t** ptr);
 
 // Dense full-context decode attention (comparator): split-K partials in a
 // workspace, then a merge.

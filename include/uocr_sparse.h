@@ -254,6 +254,30 @@ int uocr_sparse_decode_step(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32
                             float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * uocr_sparse_decode_step without a workspace, for callers that cannot
+ * allocate one: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid device allocation.  It computes exactly what
+ * uocr_sparse_decode_step computes (same kernels, same results bit for bit)
+ * and calls no allocating routine; the one launch keeps its completion
+ * counters in a static device array of the library, 256 KiB per GPU, which
+ * each GPU the library runs on holds until the process ends.
+ *   status : [1] int32 or NULL, written: 0, or 1 if a dependency wait of the
+ *            one launch gave up (the results are then undefined; never
+ *            expected).  It takes the place of the workspace's error word.
+ * Limit: when the one launch is taken (UOCR_STEP_ONE_LAUNCH, or
+ * UOCR_STEP_AUTO choosing it), n_layers * batch <= 21844;
+ * UOCR_EUNSUPPORTED beyond (pass a workspace to uocr_sparse_decode_step).
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (two streams, two threads) race and give undefined results; calls ordered
+ * on one stream are safe, each clears the counters it uses first.  Other
+ * requirements and errors as uocr_sparse_decode_step, less the workspace's.
+ */
+int uocr_sparse_decode_step_static(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n_layers,
+                                   int32_t schedule, const uint16_t* q_idx, const uint16_t* q, float* block_scores,
+                                   int32_t* block_idx, int32_t* n_sel, float* out, float* lse, int32_t* status,
+                                   void* stream);
+
+/*
  * Dense full-context decode attention, the comparator for the pages'
  * per-step speed claim against full attention (leheavengame.com OCR 2
  * release article, Sec. 1): per head h, softmax over ALL tokens 0..p of the

@@ -45,6 +45,7 @@ def test_header_declares_the_boundary():
               "uocr_page_coords", "uocr_pool_create", "uocr_pool_destroy", "uocr_pool_append", "uocr_pool_keep",
               "uocr_pool_table", "uocr_pool_used", "uocr_pool_peak", "uocr_page_window_run",
               "uocr_indexer_score_prefill", "uocr_block_topk_prefill", "uocr_sparse_attn_prefill",
+              "uocr_sparse_decode_step", "uocr_sparse_decode_step_static",
               "uocr_workspace_size", "uocr_status_string", "uocr_last_error", "uocr_abi_version"]:
         assert n in names
 
@@ -185,6 +186,32 @@ def test_decode_step_argument_checks(U):
     assert e.value.status == 5
     call(n_layers=0)                    # nothing to do: no launch, no error
     call(kv=_kv(U, batch=0), ws=None)
+
+
+def test_decode_step_static_argument_checks(U):
+    """The no-workspace decode step: the same checks as the workspace entry
+    point, and the one launch's limit of its static counters (21844
+    layer-sequence slots, i.e. 2 + 3 * 21844 <= 65536 words), all refused on
+    the host before any HIP call."""
+    cfg = U.make_cfg()
+
+    def call(kv=None, n_layers=12, schedule=U.STEP_ONE_LAUNCH, status=None, q=FAKE):
+        U.sparse_decode_step_static(cfg, kv or _kv(U), n_layers, FAKE, q, FAKE, FAKE, FAKE, status=status, stream=0,
+                                    schedule=schedule)
+
+    for kwargs, code, text in ((dict(n_layers=-1), 2, "n_layers"), (dict(q=None), 1, "q"),
+                               (dict(status=FAKE + 2), 1, "status"), (dict(schedule=7), 1, "schedule")):
+        with pytest.raises(U.UocrError) as e:
+            call(**kwargs)
+        assert e.value.status == code and text in U.last_error(), (kwargs, U.last_error())
+    with pytest.raises(U.UocrError) as e:
+        call(kv=_kv(U, batch=1), n_layers=21845)
+    assert e.value.status == 5 and "21844" in U.last_error()
+    with pytest.raises(U.UocrError) as e:   # the automatic choice takes the one launch here
+        call(kv=_kv(U, batch=4, max_blocks=14336), n_layers=5462, schedule=U.STEP_AUTO)
+    assert e.value.status == 5 and "21844" in U.last_error()
+    call(n_layers=0)
+    call(kv=_kv(U, batch=0))
 
 
 def test_dense_decode_argument_checks(U):
