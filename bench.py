@@ -519,24 +519,24 @@ def run_page_gate(U, SD, W, torch, reps=20):
     ws1 = torch.empty(U.workspace_size(cfg, U.OP_DECODE_STEP, B, M), dtype=torch.uint8, device="cuda")
     scores1 = scores.view(1, B, M)
 
-    def one_launch(kv):
+    def lib_step(kv, sched):
         U.sparse_decode_step(cfg, kv, 1, dev.q_idx, dev.q, scores1, idx.view(1, B, 16), out.view(1, B, H, 128),
-                             lse.view(1, B, H), ws=ws1, stream=sh, schedule=U.STEP_ONE_LAUNCH)
+                             lse.view(1, B, H), ws=ws1, stream=sh, schedule=sched)
 
     t_plain = timed(lambda: step(kv_plain))
     t_gate = timed(lambda: step(kv_gate))
-    t1_plain = timed(lambda: one_launch(kv_plain))
-    t1_gate = timed(lambda: one_launch(kv_gate))
+    t1_plain = timed(lambda: lib_step(kv_plain, U.STEP_ONE_LAUNCH))
+    t1_gate = timed(lambda: lib_step(kv_gate, U.STEP_ONE_LAUNCH))
+    ta_plain = timed(lambda: lib_step(kv_plain, U.STEP_AUTO))
+    ta_gate = timed(lambda: lib_step(kv_gate, U.STEP_AUTO))
     idx_b, topk_b, attn_b = decode_bytes(wl)
     step_bytes = idx_b + topk_b + attn_b
+    us = {"plain": t_plain, "page_aware": t_gate, "one_launch_plain": t1_plain, "one_launch_page_aware": t1_gate,
+          "auto_plain": ta_plain, "auto_page_aware": ta_gate}
     res["decode"] = {"workload": wl.name, "queries": B, "algorithmic_bytes": step_bytes,
-                     "us": {"plain": t_plain * 1e3, "page_aware": t_gate * 1e3,
-                            "one_launch_plain": t1_plain * 1e3, "one_launch_page_aware": t1_gate * 1e3},
-                     "query_heads_per_s": {"plain": B * H / (t_plain * 1e-3), "page_aware": B * H / (t_gate * 1e-3),
-                                           "one_launch_plain": B * H / (t1_plain * 1e-3),
-                                           "one_launch_page_aware": B * H / (t1_gate * 1e-3)},
-                     "hbm_GBps_page_aware": step_bytes / (t_gate * 1e-3) / 1e9,
-                     "hbm_GBps_one_launch_page_aware": step_bytes / (t1_gate * 1e-3) / 1e9}
+                     "us": {k: v * 1e3 for k, v in us.items()},
+                     "query_heads_per_s": {k: B * H / (v * 1e-3) for k, v in us.items()},
+                     "hbm_frac": {k: step_bytes / (v * 1e-3) / 1e9 / HBM_PEAK_GBPS for k, v in us.items()}}
     del dev, scores, out, ws1
     torch.cuda.empty_cache()
 
@@ -978,8 +978,7 @@ def main():
         log("page-aware ranking: ragged multi-page decode and the 128K prefill chunk, with and without page tags")
         result["page_gate"] = run_page_gate(U, SD, W, torch)
         pg = result["page_gate"]
-        log(f"page-aware decode {pg['decode']['us']['page_aware']:.1f} us (plain {pg['decode']['us']['plain']:.1f} us), "
-            f"one launch {pg['decode']['us']['one_launch_page_aware']:.1f} us (plain {pg['decode']['us']['one_launch_plain']:.1f} us); "
+        log("ragged decode B=64: " + ", ".join(f"{k} {v:.1f} us" for k, v in pg["decode"]["us"].items()) + "; "
             f"prefill scoring+merge {pg['prefill_scoring_and_merge']['us']['page_aware']:.1f} us "
             f"(plain {pg['prefill_scoring_and_merge']['us']['plain']:.1f} us)")
 

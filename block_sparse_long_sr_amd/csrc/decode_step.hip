@@ -240,6 +240,12 @@ DecodeStepPlan decode_step_plan(int32_t n_layers, int32_t batch, int32_t heads, 
   // 16 below 2048 blocks, so that a sequence's scoring spreads over many
   // workgroups and finishes soon after its first item starts.
   p.chunk = max_blocks >= 2048 ? kMaxStepChunk : 16;
+  // Workgroups per CU: two at long contexts; one below 2048 blocks, where a
+  // sequence's layer chain (scoring, selection, attention) rather than
+  // bandwidth sets the pace and half the bytes in flight shorten the memory
+  // latency every step of the chain sees (16 x 12 x 32K: 447-464 us against
+  // 598 us with two; at 128K two are better, 1103 against 1138 us).
+  p.groups_per_cu = max_blocks >= 2048 ? 2 : 1;
   p.counter_words = 2 + 3 * S;
   p.ws_bytes = (size_t)((p.counter_words * 4 + 255) / 256 * 256);
   p.items = S * (((int64_t)max_blocks + p.chunk - 1) / p.chunk + heads);
@@ -247,18 +253,17 @@ DecodeStepPlan decode_step_plan(int32_t n_layers, int32_t batch, int32_t heads, 
 }
 
 namespace {
-// Workgroups of the step kernel that fit on one compute unit: its launch
+// At most two workgroups of the step kernel share a compute unit: its launch
 // bounds allow 128 VGPRs per lane at 4 waves per SIMD, i.e. two 8-wave
 // workgroups, and its LDS (well under half of the 160 KB of a CU) does not
 // lower that.
-constexpr int kStepGroupsPerCu = 2;
 static_assert(sizeof(SelectSmem<kStepThreads>) + sizeof(AttendSmem<kStepThreads>) + 4 * kMaxFusedTopk +
                       4 * kMaxStepChunk + 64 <=
-                  160 * 1024 / kStepGroupsPerCu,
+                  160 * 1024 / 2,
               "two step workgroups must fit in one CU's LDS");
 
 template <int KPT>
-hipError_t launch_step(const DecodeStepArgs& a, int64_t items, hipStream_t stream) {
+hipError_t launch_step(const DecodeStepArgs& a, const DecodeStepPlan& plan, hipStream_t stream) {
   // One resident wave of workgroups (they loop over the tickets).  A grid
   // larger than what fits is also correct: a workgroup takes a ticket only
   // once it runs, so late ones find none left.
@@ -267,8 +272,8 @@ hipError_t launch_step(const DecodeStepArgs& a, int64_t items, hipStream_t strea
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const int64_t fit = (int64_t)kStepGroupsPerCu * (cus > 0 ? cus : 1);
-  const int64_t grid = items < fit ? items : fit;
+  const int64_t fit = (int64_t)plan.groups_per_cu * (cus > 0 ? cus : 1);
+  const int64_t grid = plan.items < fit ? plan.items : fit;
   hipLaunchKernelGGL(decode_step_kernel<KPT>, dim3((unsigned)grid), dim3(kStepThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -377,8 +382,8 @@ hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& pla
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t max_cand = (int64_t)a.max_blocks - a.local_blocks;
-  if (max_cand <= kStepThreads * 8) return launch_step<8>(a, plan.items, stream);
-  if (max_cand <= kStepThreads * 32) return launch_step<32>(a, plan.items, stream);
+  if (max_cand <= kStepThreads * 8) return launch_step<8>(a, plan, stream);
+  if (max_cand <= kStepThreads * 32) return launch_step<32>(a, plan, stream);
   return hipErrorInvalidValue;
 }
 

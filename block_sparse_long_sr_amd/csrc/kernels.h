@@ -128,6 +128,7 @@ struct DecodeStepPlan {
   int32_t chunk;          // blocks per scoring item
   int64_t counter_words;  // 2 + 3 * n_layers * batch
   int64_t items;          // work items of the launch
+  int32_t groups_per_cu;  // resident workgroups per compute unit
   size_t ws_bytes;
 };
 DecodeStepPlan decode_step_plan(int32_t n_layers, int32_t batch, int32_t heads, int32_t max_blocks);
