@@ -42,14 +42,14 @@ struct WsView {
   int32_t* off;    // [M+1] first pair of each block's bucket
   int32_t* choff;  // [M+1] first chunk of each block; choff[M] = number of chunks
   int32_t* pairs;  // [T*topk] flat pair indices t*topk + s, bucketed by block
-  int32_t* chunk;  // [max_chunks] block of each chunk
+  int4* desc;      // [max_chunks] chunk descriptors: block j (-1: no chunk), first pair, rows, pool block
   float* part;     // [T][H][topk][kPartStride]
 };
 
 __device__ __forceinline__ WsView ws_view(const PrefillAttnArgs& a) {
   unsigned char* w = static_cast<unsigned char*>(a.ws);
   return {reinterpret_cast<int32_t*>(w + a.plan.off_off), reinterpret_cast<int32_t*>(w + a.plan.choff_off),
-          reinterpret_cast<int32_t*>(w + a.plan.pairs_off), reinterpret_cast<int32_t*>(w + a.plan.chunk_off),
+          reinterpret_cast<int32_t*>(w + a.plan.pairs_off), reinterpret_cast<int4*>(w + a.plan.chunk_off),
           reinterpret_cast<float*>(w + a.plan.part_off)};
 }
 
@@ -163,7 +163,11 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
     const int nch = (c + kRowsPerChunk - 1) / kRowsPerChunk;
     w.off[j] = po;
     w.choff[j] = co;
-    for (int q = 0; q < nch; ++q) w.chunk[co + q] = j;
+    if (nch > 0) {
+      const int pb = A.block_table[j];  // sequence 0
+      for (int q = 0; q < nch; ++q)
+        w.desc[co + q] = make_int4(j, po + q * kRowsPerChunk, min(kRowsPerChunk, c - q * kRowsPerChunk), pb);
+    }
     s_cnt[j] = po;  // becomes the bucket's cursor
     po += c;
     co += nch;
@@ -172,6 +176,9 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
     w.off[M] = s_scan[0][kBucketThreads - 1];
     w.choff[M] = s_scan[1][kBucketThreads - 1];
   }
+  // descriptors past the last chunk: none
+  for (int g = s_scan[1][kBucketThreads - 1] + tid; g < a.plan.max_chunks; g += kBucketThreads)
+    w.desc[g] = make_int4(-1, 0, 0, -1);
   __syncthreads();
   if constexpr (STAGE > 0) {
     // s_cnt now holds each bucket's first position; start + rank stays below
@@ -216,11 +223,14 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel
   const int64_t unit = (int64_t)blockIdx.x * kBlockWaves + wave;
   const int g = (int)(unit / A.heads);
   const int h = (int)(unit - (int64_t)g * A.heads);
-  if (g >= w.choff[A.max_blocks]) return;
-  const int j = w.chunk[g];
-  const int start = w.off[j] + (g - w.choff[j]) * kRowsPerChunk;
-  const int n_rows = min(kRowsPerChunk, w.off[j + 1] - start);
-  const int pb = A.block_table[j];  // sequence 0
+  if (g >= a.plan.max_chunks) return;
+  // one descriptor read, then the tiles and this lane's pair load together
+  const int4 d = w.desc[g];
+  const int j = __builtin_amdgcn_readfirstlane(d.x);
+  if (j < 0) return;
+  const int start = __builtin_amdgcn_readfirstlane(d.y);
+  const int n_rows = __builtin_amdgcn_readfirstlane(d.z);
+  const int pb = __builtin_amdgcn_readfirstlane(d.w);
   const bool ok = pb >= 0 && (int64_t)pb < A.num_blocks;
   const int lane = lane_id();
   const int n = lane & 31;
@@ -237,15 +247,16 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel
     const uint16_t* kt = A.k_pool + tile;
     const uint16_t* vt = A.v_pool + tile;
     const uint16_t* qr = A.q + ((int64_t)t_n * A.heads + h) * kDim;
+    // K and V depend only on the descriptor: issued first, while this
+    // lane's pair (and with it the row of q) is still in flight
     bf16x8_t av[8], bq[8];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      av[st] = *reinterpret_cast<const bf16x8_t*>(kt + n * kDim + 64 * hh + 8 * st);
-      bq[st] = *reinterpret_cast<const bf16x8_t*>(qr + 64 * hh + 8 * st);
-    }
+    for (int st = 0; st < 8; ++st) av[st] = *reinterpret_cast<const bf16x8_t*>(kt + n * kDim + 64 * hh + 8 * st);
     uint32_t vw[kBlock];
 #pragma unroll
     for (int k = 0; k < kBlock; ++k) vw[k] = reinterpret_cast<const uint32_t*>(vt + k * kDim)[lane];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) bq[st] = *reinterpret_cast<const bf16x8_t*>(qr + 64 * hh + 8 * st);
     f32x16_t c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[0], bq[0], f32x16_t{0}, 0, 0, 0);
 #pragma unroll
     for (int st = 1; st < 8; ++st) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[st], bq[st], c, 0, 0, 0);
@@ -390,7 +401,7 @@ PrefillAttnPlan prefill_attn_plan(int32_t T, int32_t heads, int32_t topk, int32_
   p.pairs_off = at;
   at = align256(at + (size_t)npairs * 4);
   p.chunk_off = at;
-  at = align256(at + (size_t)p.max_chunks * 4);
+  at = align256(at + (size_t)p.max_chunks * 16);
   p.part_off = at;
   at = align256(at + (size_t)npairs * heads * kPartStride * 4);
   p.ws_bytes = at;

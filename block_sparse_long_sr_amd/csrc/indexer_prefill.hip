@@ -400,8 +400,48 @@ hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t strea
 // Merge of the per-split lists (SR-SWA step 3 for prefill rows): one wave per
 // row, lane s holds split s's sorted list; R rounds of a wave-wide arg-max on
 // the composite (key, -id) pick the remote blocks in rank order, which are
-// then written ascending, followed by the row's local window.
+// then written ascending, followed by the row's local window.  The arg-max
+// runs on DPP row operations and the gfx950 lane swaps (a quad, the two
+// halves of a row, the two halves of each 16-lane row, lanes l ^ 16 and
+// l ^ 32), not LDS permutes, so a round is a short chain of VALU ops.
 // ---------------------------------------------------------------------------
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false);
+}
+
+// Larger of (hi, lo) and the pair another lane holds, compared as one 64-bit
+// value.
+__device__ __forceinline__ void take_larger(uint32_t& hi, uint32_t& lo, uint32_t ohi, uint32_t olo) {
+  const bool take = ohi > hi || (ohi == hi && olo > lo);
+  hi = take ? ohi : hi;
+  lo = take ? olo : lo;
+}
+
+// Every lane gets the wave's largest (hi, lo).
+__device__ __forceinline__ void wave_max_pair(uint32_t& hi, uint32_t& lo) {
+  take_larger(hi, lo, dpp_u32<0xB1>(hi), dpp_u32<0xB1>(lo));    // quad_perm [1,0,3,2]
+  take_larger(hi, lo, dpp_u32<0x4E>(hi), dpp_u32<0x4E>(lo));    // quad_perm [2,3,0,1]
+  take_larger(hi, lo, dpp_u32<0x141>(hi), dpp_u32<0x141>(lo));  // row_half_mirror
+  take_larger(hi, lo, dpp_u32<0x140>(hi), dpp_u32<0x140>(lo));  // row_mirror
+  {
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    uint32_t h0 = h[0], l0 = l[0];
+    take_larger(h0, l0, h[1], l[1]);
+    hi = h0;
+    lo = l0;
+  }
+  {
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    uint32_t h0 = h[0], l0 = l[0];
+    take_larger(h0, l0, h[1], l[1]);
+    hi = h0;
+    lo = l0;
+  }
+}
 
 template <int R>
 __global__ __launch_bounds__(256) void topk_prefill_kernel(TopkPrefillArgs a) {
@@ -422,14 +462,33 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(TopkPrefillArgs a) {
   if constexpr (R > 0) {
   // Lane s holds split s's list, decoded into (truncated score, id) pairs.
   const uint32_t idmask = (1u << P.idbits) - 1u;
+  uint32_t kp[R];
+  const size_t off = ((size_t)lane * a.T + t) * R;  // [nsplit][T][R]
+  if (lane < P.nsplit) {
+    if constexpr (R % 4 == 0) {  // 16-byte aligned lists: R / 4 vector loads
+      const uint4* src = reinterpret_cast<const uint4*>(a.cand_keys + off);
+#pragma unroll
+      for (int r4 = 0; r4 < R / 4; ++r4) {
+        const uint4 v = src[r4];
+        kp[4 * r4] = v.x;
+        kp[4 * r4 + 1] = v.y;
+        kp[4 * r4 + 2] = v.z;
+        kp[4 * r4 + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) kp[r] = a.cand_keys[off + r];
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) kp[r] = 0u;
+  }
   uint32_t lk[R];
   int32_t li[R];
-  const size_t off = ((size_t)lane * a.T + t) * R;  // [nsplit][T][R]
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const uint32_t kp = lane < P.nsplit ? a.cand_keys[off + r] : 0u;
-    lk[r] = kp >> P.idbits;  // >= 1 for every real candidate
-    li[r] = kp != 0u ? lane * P.bps + (int32_t)(idmask - (kp & idmask)) : -1;
+    lk[r] = kp[r] >> P.idbits;  // >= 1 for every real candidate
+    li[r] = kp[r] != 0u ? lane * P.bps + (int32_t)(idmask - (kp[r] & idmask)) : -1;
   }
 
   int32_t mine = -1;  // lane w keeps the w-th winner
@@ -439,14 +498,7 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(TopkPrefillArgs a) {
     uint32_t hi = li[0] >= 0 ? lk[0] : 0u;
     uint32_t lo = li[0] >= 0 ? 0xFFFFFFFFu - (uint32_t)li[0] : 0u;
     const uint32_t my_hi = hi, my_lo = lo;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-      const uint32_t ohi = __shfl_xor(hi, m, kWave);
-      const uint32_t olo = __shfl_xor(lo, m, kWave);
-      const bool take = ohi > hi || (ohi == hi && olo > lo);
-      hi = take ? ohi : hi;
-      lo = take ? olo : lo;
-    }
+    wave_max_pair(hi, lo);
     if (hi == 0u && lo == 0u) break;
     const int32_t id = (int32_t)(0xFFFFFFFFu - lo);
     if (lane == w) mine = id;
@@ -463,8 +515,9 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(TopkPrefillArgs a) {
 
   // Ascending order of the R winners: rank by counting smaller ids.
   int rank = 0;
+#pragma unroll
   for (int v = 0; v < R; ++v) {
-    const int32_t other = __shfl(mine, v, kWave);
+    const int32_t other = __builtin_amdgcn_readlane(mine, v);
     rank += (other < mine) ? 1 : 0;
   }
   if (lane < R && mine >= 0) out[rank] = mine;

@@ -215,6 +215,12 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
  *     are taken in a fixed ticket order by a grid that stays resident; a
  *     sequence's selection and attention start as soon as its own scoring is
  *     done, overlapping the scoring of other sequences, with no launch gaps.
+ *     It needs every layer's q and q_idx in memory before it starts: it
+ *     keeps the layer order of each sequence, but it cannot wait for a
+ *     layer's queries to be produced from the previous layer's output.  A
+ *     model that computes layer l + 1's queries from layer l's attention
+ *     calls the step once per layer (n_layers = 1), which runs the per-layer
+ *     launches below.
  *   UOCR_STEP_PER_LAYER: per layer, the scoring launch and the fused
  *     selection + attention launch of uocr_topk_attn_decode.
  *   UOCR_STEP_AUTO: the one launch when n_layers >= 2 and batch * max_blocks
