@@ -205,8 +205,9 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
 
 // One wave per (chunk, head).  Lane l works on chunk row n = l % 32 and
 // half hh = l / 32 for the scores, and on output dims 2l, 2l+1 for P.V.
-//  * A fragment of step s (dims 64 hh + 8 s .. +8, the summation-order
-//    permutation shared by A and B): K row n; B fragment: q of chunk row n
+//  * A fragment of step s (dims 16 s + 8 hh .. +8, the summation-order
+//    permutation shared by A and B, so the two lanes of a row read 32
+//    adjacent bytes): K row n; B fragment: q of chunk row n
 //    (rows past the chunk repeat row 0; their results are never used).
 //  * C register r of lane l holds the score of key 8 (r / 4) + 4 hh + r % 4
 //    for chunk row n.
@@ -251,12 +252,12 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel
     // lane's pair (and with it the row of q) is still in flight
     bf16x8_t av[8], bq[8];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) av[st] = *reinterpret_cast<const bf16x8_t*>(kt + n * kDim + 64 * hh + 8 * st);
+    for (int st = 0; st < 8; ++st) av[st] = *reinterpret_cast<const bf16x8_t*>(kt + n * kDim + 16 * st + 8 * hh);
     uint32_t vw[kBlock];
 #pragma unroll
     for (int k = 0; k < kBlock; ++k) vw[k] = reinterpret_cast<const uint32_t*>(vt + k * kDim)[lane];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) bq[st] = *reinterpret_cast<const bf16x8_t*>(qr + 64 * hh + 8 * st);
+    for (int st = 0; st < 8; ++st) bq[st] = *reinterpret_cast<const bf16x8_t*>(qr + 16 * st + 8 * hh);
     f32x16_t c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[0], bq[0], f32x16_t{0}, 0, 0, 0);
 #pragma unroll
     for (int st = 1; st < 8; ++st) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[st], bq[st], c, 0, 0, 0);

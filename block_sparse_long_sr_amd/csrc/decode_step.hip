@@ -49,6 +49,7 @@ constexpr int kStepThreads = 512;
 constexpr int kStepWaves = kStepThreads / kWave;
 constexpr int kMaxStepChunk = 32;  // blocks per scoring item, at most
 constexpr uint32_t kSpinLimit = 1u << 20;  // polls of one wait: a device-scope load (~1 us) + s_sleep 2 each, about a second
+constexpr int kTableCache = 4096;  // block-table rows up to this many entries are read into LDS
 
 struct Item {
   int attention;  // 0: scoring item, 1: attention item
@@ -116,6 +117,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
   __shared__ SelectSmem<kStepThreads> sel_sm;
   __shared__ AttendSmem<kStepThreads> att_sm;
   __shared__ int32_t s_blocks[kMaxFusedTopk];
+  __shared__ int32_t s_table[kTableCache];
   __shared__ uint32_t s_ticket;
   __shared__ int s_last;
   __shared__ float s_chunk[kMaxStepChunk];  // an item's block scores
@@ -152,21 +154,26 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
     const int32_t* table = a.block_table + (int64_t)b * M;
 
     if (!it.attention) {
+      const int j0 = it.idx * chunk;
+      const int jend_all = min(j0 + chunk, M);
+      const int jend = min(jend_all, ncand);
+      // the pool indices of the wave's first two blocks are read before the
+      // wait for the previous layer (the table does not depend on it)
+      const int jA = j0 + wave, jB = jA + kStepWaves;
+      const int pbA = jA < jend ? __builtin_amdgcn_readfirstlane(table[jA]) : -1;
+      const int pbB = jB < jend ? __builtin_amdgcn_readfirstlane(table[jB]) : -1;
       if (l > 0) {
         if (tid == 0) wait_count(attn_done + (it.slot - B), (uint32_t)H, err, a.status_out);
         __syncthreads();
       }
-      const int j0 = it.idx * chunk;
-      const int jend_all = min(j0 + chunk, M);
-      const int jend = min(jend_all, ncand);
       if (j0 < jend) {
         const uint4 qv = *reinterpret_cast<const uint4*>(a.q_idx + (int64_t)it.slot * kDim + (lane & 15) * 8);
         const uint16_t* kidx = a.kidx_pool + (int64_t)l * a.kidx_layer_stride;
         // blocks j and j + kStepWaves of the wave are loaded together
-        for (int j = j0 + wave; j < jend; j += 2 * kStepWaves) {
+        for (int j = jA; j < jend; j += 2 * kStepWaves) {
           const int j2 = j + kStepWaves;
-          const int pb = __builtin_amdgcn_readfirstlane(table[j]);
-          const int pb2 = j2 < jend ? __builtin_amdgcn_readfirstlane(table[j2]) : -1;
+          const int pb = j == jA ? pbA : __builtin_amdgcn_readfirstlane(table[j]);
+          const int pb2 = j == jA ? pbB : (j2 < jend ? __builtin_amdgcn_readfirstlane(table[j2]) : -1);
           const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
           const bool ok2 = pb2 >= 0 && (int64_t)pb2 < a.num_blocks;
           uint4 kv[8], kv2[8];
@@ -207,6 +214,11 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
         if (tid == 0) count_done(sel_done + it.slot);
       }
     } else {
+      // the sequence's table row goes to LDS while the selection is awaited,
+      // so the kept ids are followed by one memory round trip (the tiles)
+      const bool cached = M <= kTableCache;
+      if (cached)
+        for (int i = tid; i < M; i += kStepThreads) s_table[i] = table[i];
       if (tid == 0) wait_count(sel_done + it.slot, 1u, err, a.status_out);
       __syncthreads();
       for (int i = tid; i < a.topk; i += kStepThreads) s_blocks[i] = sel_out[i];
@@ -214,7 +226,8 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
       const int h = it.idx;
       const int64_t head_row = (int64_t)it.slot * H + h;
       const int64_t kv_off = (int64_t)l * a.kv_layer_stride;
-      attend_query_wg<kStepThreads, true>(a.k_pool + kv_off, a.v_pool + kv_off, table, a.num_blocks, H, h, M,
+      attend_query_wg<kStepThreads, true>(a.k_pool + kv_off, a.v_pool + kv_off, cached ? s_table : table,
+                                          a.num_blocks, H, h, M,
                                           L - 1, a.q + head_row * kDim, s_blocks, a.topk, a.scale_log2,
                                           a.out + head_row * kDim, a.lse != nullptr ? a.lse + head_row : nullptr,
                                           att_sm);
@@ -258,7 +271,7 @@ namespace {
 // workgroups, and its LDS (well under half of the 160 KB of a CU) does not
 // lower that.
 static_assert(sizeof(SelectSmem<kStepThreads>) + sizeof(AttendSmem<kStepThreads>) + 4 * kMaxFusedTopk +
-                      4 * kMaxStepChunk + 64 <=
+                      4 * kTableCache + 4 * kMaxStepChunk + 64 <=
                   160 * 1024 / 2,
               "two step workgroups must fit in one CU's LDS");
 
