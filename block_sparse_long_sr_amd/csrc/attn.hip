@@ -36,8 +36,10 @@ int attn_threads(int64_t workgroups) {
 
 // Attention of query qi, head h over the kept blocks in sel[0 .. topk)
 // (global or LDS memory); every thread of the NT-thread workgroup calls it.
+// `row` (global or LDS), when given, is the query's block-table row.
 template <int NT>
-__device__ __forceinline__ void attend_query(const AttnArgs& a, int qi, int h, const int32_t* sel) {
+__device__ __forceinline__ void attend_query(const AttnArgs& a, int qi, int h, const int32_t* sel,
+                                             const int32_t* row = nullptr) {
   __shared__ AttendSmem<NT> sm;
   int seq, p;
   if (a.prefill) {
@@ -48,7 +50,7 @@ __device__ __forceinline__ void attend_query(const AttnArgs& a, int qi, int h, c
     p = clamp_ctx(a.ctx_lens[qi], a.max_blocks) - 1;
   }
   const int64_t head_row = (int64_t)qi * a.heads + h;
-  const int32_t* table = a.block_table + (int64_t)seq * a.max_blocks;
+  const int32_t* table = row != nullptr ? row : a.block_table + (int64_t)seq * a.max_blocks;
   float* lse = a.lse != nullptr ? a.lse + head_row : nullptr;
   if (a.prefill)  // rows of a chunk share tiles: cached loads
     attend_query_wg<NT, false>(a.k_pool, a.v_pool, table, a.num_blocks, a.heads, h, a.max_blocks, p,
@@ -70,10 +72,16 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
 // workgroup also writes the selection out.  This saves the separate
 // selection launch and its drain/fill gap between the scoring and attention
 // launches of a layer.
+// The sequence's block-table row is copied to LDS (rows up to
+// kFusedTableCache entries) while the scores are read and ranked, so the
+// kept ids are followed by one memory round trip, the K and V tiles.
+constexpr int kFusedTableCache = 4096;
+
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void select_attn_kernel(SelAttnArgs sa) {
   __shared__ SelectSmem<NT> sm;
   __shared__ int32_t s_blocks[kMaxFusedTopk];
+  __shared__ int32_t s_table[kFusedTableCache];
   const AttnArgs& a = sa.attn;
   const int b = blockIdx.x;
   const int h = blockIdx.y;
@@ -81,6 +89,11 @@ __global__ __launch_bounds__(NT) void select_attn_kernel(SelAttnArgs sa) {
   const int nb = (L + kBlock - 1) / kBlock;
   const int ncand = nb - sa.local_blocks > 0 ? nb - sa.local_blocks : 0;
   const int R = a.topk - sa.local_blocks;
+  const bool cached = a.max_blocks <= kFusedTableCache;
+  if (cached) {
+    const int32_t* row = a.block_table + (int64_t)b * a.max_blocks;
+    for (int i = threadIdx.x; i < nb; i += NT) s_table[i] = row[i];
+  }
   if (!select_trivial(nb, ncand, R, a.topk, s_blocks, NT))
     select_sorted_reg<NT, KPT>(sa.block_scores + (int64_t)b * a.max_blocks, ncand, R, sa.local_blocks, s_blocks, sm,
                                sa.block_page != nullptr ? sa.block_page + (int64_t)b * a.max_blocks : nullptr,
@@ -90,7 +103,7 @@ __global__ __launch_bounds__(NT) void select_attn_kernel(SelAttnArgs sa) {
     for (int i = threadIdx.x; i < a.topk; i += NT) sa.block_idx_out[(int64_t)b * a.topk + i] = s_blocks[i];
     if (sa.n_sel != nullptr && threadIdx.x == 0) sa.n_sel[b] = nb < a.topk ? nb : a.topk;
   }
-  attend_query<NT>(a, b, h, s_blocks);
+  attend_query<NT>(a, b, h, s_blocks, cached ? s_table : nullptr);
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
