@@ -426,8 +426,12 @@ def run_prefill(U, SD, W, torch, iters=5):
         "ms": {"scoring": t_sc, "merge": t_mg, "attention": t_at, "scoring_back_to_back": t_sc_alone},
         "scoring_back_to_back_batches_ms": batches,
         "scoring_in_step_TFLOPs": flops / (t_sc * 1e-3) / 1e12,
+        # frac: the kernel in steady state (back-to-back batches above);
+        # frac_in_step: the same FLOPs over the scoring launch as timed inside
+        # the chunk step (one launch between the attention and the merge).
         "scoring_roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS,
+                             "frac_in_step": flops / (t_sc * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                              "flops_per_launch": flops, "traffic": traffic_for("indexer_prefill")},
         "attention_gathered_GBps": T * 2 * 512 * 10 * 128 * 2 / (t_at * 1e-3) / 1e9,
         "attention_unique_bytes_upper": attn_unique,
