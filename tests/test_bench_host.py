@@ -1,6 +1,7 @@
 """Host checks of bench.py that need no GPU: the algorithmic bytes behind
 the decode roofline, counted from the method's steps (news.rkmt.cn/news/25027
-Sec. 5) with the oracle's block bookkeeping, and the one-GPU guard."""
+Sec. 5) with the oracle's block bookkeeping, the band rule of the bench's
+parity record, and the one-GPU guard."""
 import importlib.util
 import os
 import subprocess
@@ -60,3 +61,72 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2
     assert "exactly one GPU" in r.stderr
+
+
+def _tiny_query(seed=7, L=1500, H=10, D=128):
+    """One decode query over an L-token context (47 blocks) from the synth
+    generator's bf16 rounding; K/V fetched from host arrays."""
+    import numpy as np
+    g = np.random.default_rng(seed)
+
+    def bf16(x):
+        b = np.asarray(x, np.float32).view(np.uint32)
+        return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+    q, qi = bf16(g.standard_normal((H, D))), bf16(g.standard_normal(D))
+    kidx = bf16(g.standard_normal((L, D)))
+    k, v = bf16(g.standard_normal((H, L, D))), bf16(g.standard_normal((H, L, D)))
+    fetch = lambda toks: (k[:, toks, :], v[:, toks, :])
+    return q, qi, kidx, fetch, L
+
+
+def test_parity_tally_band_rule():
+    """The bench's parity record: the oracle's own result is exact; a GPU
+    selection that swaps the cutoff block for an unselected block whose score
+    lies within the 1e-4 band is accepted (its attention is checked against
+    the oracle recomputed on that set), outside the band it is a mismatch;
+    attention off by more than the tolerance fails."""
+    import numpy as np
+    bench = _bench()
+    cfg = oracle.SparseCfg()
+    q, qi, kidx, fetch, L = _tiny_query()
+    p = L - 1
+    ref = oracle.decode_query_fetch(q, qi, kidx, fetch, L, cfg)
+    sel = ref["selected"]
+    idx_row = np.array(sel + [-1] * (cfg.topk_blocks - len(sel)), np.int32)
+
+    t = bench.ParityTally()
+    t.add("exact", ref, idx_row, ref["out"].astype(np.float32), ref["lse"].astype(np.float32), q, fetch, p, cfg)
+    assert t.record()["pass"] and t.exact == 1
+
+    # the remote block at the cutoff, and the best unselected candidate
+    remote = [j for j in sel if j not in ref["local"]]
+    bs = ref["block_scores"].astype(np.float64)
+    j_cut = min(remote, key=lambda j: (bs[j], -j))
+    out_blocks = [j for j in range(oracle.candidate_count(p, cfg)) if j not in sel]
+    j_in = max(out_blocks, key=lambda j: bs[j])
+    got = sorted(set(sel) - {j_cut} | {j_in})
+    toks = oracle.attended_tokens(got, p, cfg)
+    k, v = fetch(toks)
+    o2, l2 = oracle.attend(q, k, v, np.arange(toks.size), cfg.sm_scale)
+    row = np.array(got + [-1] * (cfg.topk_blocks - len(got)), np.int32)
+
+    near = dict(ref)
+    near["block_scores"] = ref["block_scores"].copy()
+    near["block_scores"][j_in] = np.float32(ref["cutoff"] * (1 - 5e-5 * np.sign(ref["cutoff"])))
+    t = bench.ParityTally()
+    t.add("in band", near, row, o2.astype(np.float32), l2.astype(np.float32), q, fetch, p, cfg)
+    r = t.record()
+    assert r["pass"] and r["selection_differences_inside_band"] == 1, r
+
+    t = bench.ParityTally()
+    t.add("outside band", ref, row, o2.astype(np.float32), l2.astype(np.float32), q, fetch, p, cfg)
+    r = t.record()
+    assert not r["pass"] and r["selection_mismatches_outside_band"] == 1
+
+    bad = ref["out"].astype(np.float32).copy()
+    bad[3, 5] += 5e-3
+    t = bench.ParityTally()
+    t.add("attention", ref, idx_row, bad, ref["lse"].astype(np.float32), q, fetch, p, cfg)
+    r = t.record()
+    assert not r["pass"] and r["attention_on_gpu_selection"]["max_abs"] > 4e-3
