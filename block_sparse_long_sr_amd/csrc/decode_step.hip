@@ -4,7 +4,9 @@
 // Sec. 5).
 //
 // Work items, handed out in ticket order by one atomic counter (a workgroup
-// takes its next ticket while it works on the current item):
+// takes its next ticket as it publishes the current item's results, so the
+// request's round trip overlaps the stores' and items start in about the
+// order of their tickets):
 //   * scoring item (layer l, sequence b, chunk c): `chunk` blocks of the
 //     sequence's candidates, two 8 KB blocks per wave in flight.  The
 //     workgroup that completes the last chunk of (l, b) then runs the
@@ -98,6 +100,16 @@ __device__ __forceinline__ void publish(T* p, T v) {
 // until the wave's own stores have completed (a barrier alone does not).
 __device__ __forceinline__ void drain_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Thread 0: the next work item's ticket.  A workgroup asks for it while
+// publishing its current item (after the result stores, before their
+// drain), not when the item starts: a ticket taken one item ahead would
+// start up to a whole item (5-25 us) after it was handed out, spreading one
+// sequence's scoring items over that much time and lengthening its layer
+// chain (16 x 12 x 32K: 427 against 452 us).
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* ticket) {
+  return __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Thread 0, after drain_stores and a barrier: count one completion; returns
 // the count before it.
 __device__ __forceinline__ uint32_t count_done(uint32_t* ctr) {
@@ -137,12 +149,11 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
   uint32_t* sel_done = score_done + S;
   uint32_t* attn_done = sel_done + S;
 
-  if (tid == 0) s_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) s_ticket = take_ticket(ticket);
   __syncthreads();
   uint32_t t = s_ticket;
   while (t < total) {
-    __syncthreads();  // every thread has read s_ticket
-    if (tid == 0) s_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t next_t = 0;  // thread 0: the ticket of the next item
     const Item it = item_of(t, S, C, H, D);
     const int l = it.slot / B;
     const int b = it.slot - l * B;
@@ -191,6 +202,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
       // one coalesced store of the item's scores (non-candidates: -inf)
       for (int j = j0 + tid; j < jend_all; j += kStepThreads)
         publish(scores + j, j < jend ? s_chunk[j - j0] : -INFINITY);
+      if (tid == 0) next_t = take_ticket(ticket);
       drain_stores();
       __syncthreads();
       if (tid == 0) {
@@ -231,10 +243,12 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
                                           L - 1, a.q + head_row * kDim, s_blocks, a.topk, a.scale_log2,
                                           a.out + head_row * kDim, a.lse != nullptr ? a.lse + head_row : nullptr,
                                           att_sm);
+      if (tid == 0) next_t = take_ticket(ticket);
       drain_stores();
       __syncthreads();
       if (tid == 0) count_done(attn_done + it.slot);
     }
+    if (tid == 0) s_ticket = next_t;
     __syncthreads();  // the next ticket is in s_ticket; LDS of this item is free
     t = s_ticket;
   }
@@ -326,11 +340,16 @@ bool decode_step_one_launch(int32_t n_layers, int32_t batch, int32_t max_blocks)
   // scoring of others, but a sequence's layers stay in order: each layer of
   // a sequence must be scored, selected and attended within the time the
   // other sequences' scoring of that layer takes, about batch * max_blocks *
-  // 8 KB at HBM rate.  Measured at 16 sequences x 12 layers: per-layer
-  // launches win up to 64K tokens (2048 blocks), the two are even at 96K
-  // (3072 blocks) and the one launch wins at 128K; with one layer there is
-  // no layer order to overlap.
-  return n_layers >= 2 && (int64_t)batch * max_blocks >= 57344;
+  // 8 KB at HBM rate, and the first and last layers run with little to
+  // overlap.  Measured (us per step, one launch against per-layer launches,
+  // 12 layers): 16 sequences at 16K 375/332, 24K 397/400, 32K 443/468, 64K
+  // 715/713, 96K 868/959; 8 at 64K 512/447, 8 at 128K 680/716; 4 at 128K
+  // 486/450; 32 at 16K 531/550; 64 at 4K 528/560; 16 x 32K with 2 and 4
+  // layers 96/78 and 162/155.  Hence: at least 8 layers, and enough blocks
+  // in the batch for the sequence's size.
+  const int64_t blocks = (int64_t)batch * max_blocks;
+  return n_layers >= 8 &&
+         (blocks >= 32768 || (batch >= 16 && blocks >= 16384) || (batch >= 32 && blocks >= 8192));
 }
 
 hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& plan, bool one_launch,
