@@ -34,7 +34,7 @@ constexpr int kPStride = 36;                    // P row stride in LDS (floats),
 constexpr int kMergeWaves = 4;
 constexpr int kPairUnroll = 32;                 // pairs per thread kept in registers by the bucket pass
 constexpr int kPairTail = 4;                    // pairs per thread and round beyond those
-constexpr int kPartStride = kDim + 4;           // o[128], m, l, pad: 528 B per (row, head, slot)
+constexpr int kPartStride = kDim;               // o[128]: 512 B (four whole cache lines) per (row, head, slot)
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -43,14 +43,15 @@ struct WsView {
   int32_t* choff;  // [M+1] first chunk of each block; choff[M] = number of chunks
   int32_t* pairs;  // [T*topk] flat pair indices t*topk + s, bucketed by block
   int4* desc;      // [max_chunks] chunk descriptors: block j (-1: no chunk), first pair, rows, pool block
-  float* part;     // [T][H][topk][kPartStride]
+  float* part;     // [T][H][topk][kPartStride] unnormalised outputs o
+  float2* ml;      // [T][H][topk] (m, l): the 16 slots of a (row, head) share one cache line
 };
 
 __device__ __forceinline__ WsView ws_view(const PrefillAttnArgs& a) {
   unsigned char* w = static_cast<unsigned char*>(a.ws);
   return {reinterpret_cast<int32_t*>(w + a.plan.off_off), reinterpret_cast<int32_t*>(w + a.plan.choff_off),
           reinterpret_cast<int32_t*>(w + a.plan.pairs_off), reinterpret_cast<int4*>(w + a.plan.chunk_off),
-          reinterpret_cast<float*>(w + a.plan.part_off)};
+          reinterpret_cast<float*>(w + a.plan.part_off), reinterpret_cast<float2*>(w + a.plan.ml_off)};
 }
 
 __device__ __forceinline__ bool slot_counts(int j, int p, int max_blocks) {
@@ -298,8 +299,7 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel
   // (m, l) of chunk row n, written by its lane in the lower half.
   if (hh == 0 && n < n_rows) {
     const int s_n = pair_v - t_n * A.topk;
-    float* dst = w.part + (((int64_t)t_n * A.heads + h) * A.topk + s_n) * kPartStride;
-    *reinterpret_cast<float2*>(dst + kDim) = make_float2(m_row, l_row);
+    w.ml[((int64_t)t_n * A.heads + h) * A.topk + s_n] = make_float2(m_row, l_row);
   }
   for (int r = 0; r < n_rows; ++r) {
     const int i = __builtin_amdgcn_readlane(pair_v, r);
@@ -334,13 +334,14 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void attn_prefill_merge_kernel
   const int lane = lane_id();
   const int32_t* sel = A.block_idx + (int64_t)t * A.topk;
   const float* base = w.part + (int64_t)item * A.topk * kPartStride;
+  const float2* mls = w.ml + (int64_t)item * A.topk;
 
   float res0 = 0.0f, res1 = 0.0f, L = 0.0f, M = -INFINITY;
   for (int s0 = 0; s0 < A.topk; s0 += kWave) {  // one round for topk <= 64
     const int s = s0 + lane;
     const bool valid = s < A.topk && slot_counts(sel[s], p, A.max_blocks);
     float2 ml = make_float2(-INFINITY, 0.0f);
-    if (valid) ml = *reinterpret_cast<const float2*>(base + (int64_t)s * kPartStride + kDim);
+    if (valid) ml = mls[s];
     float Mr = ml.x;
 #pragma unroll
     for (int m_ = 1; m_ < kWave; m_ <<= 1) Mr = fmaxf(Mr, __shfl_xor(Mr, m_, kWave));
@@ -405,6 +406,8 @@ PrefillAttnPlan prefill_attn_plan(int32_t T, int32_t heads, int32_t topk, int32_
   at = align256(at + (size_t)p.max_chunks * 16);
   p.part_off = at;
   at = align256(at + (size_t)npairs * heads * kPartStride * 4);
+  p.ml_off = at;
+  at = align256(at + (size_t)npairs * heads * 8);
   p.ws_bytes = at;
   return p;
 }
