@@ -205,18 +205,26 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
 }
 
 // One wave per (chunk, head).  Lane l works on chunk row n = l % 32 and
-// half hh = l / 32 for the scores, and on output dims 2l, 2l+1 for P.V.
+// half hh = l / 32 for the scores.
 //  * A fragment of step s (dims 16 s + 8 hh .. +8, the summation-order
 //    permutation shared by A and B, so the two lanes of a row read 32
 //    adjacent bytes): K row n; B fragment: q of chunk row n
 //    (rows past the chunk repeat row 0; their results are never used).
 //  * C register r of lane l holds the score of key 8 (r / 4) + 4 hh + r % 4
 //    for chunk row n.
-//  * P goes through a wave-private LDS tile [32 rows][kPStride]; each output
-//    row then reads its 32 probabilities (broadcast reads) against the lane's
-//    two V columns, kept in fp32.  V of keys past every row's position is
-//    replaced by 0 (such slots may hold anything, NaN included, and a masked
-//    key's probability 0 must not meet it).
+//  * P goes through a wave-private LDS tile [32 rows][kPStride].
+//  * V is read with eight 1 KB-contiguous non-temporal loads (each reads
+//    whole cache lines once, so V does not displace other lines from the
+//    caches): lane l holds dims 8 (l % 16) .. +8 of keys 4 i + kg, i = 0..7,
+//    kg = l / 16, widened to fp32 once.  V of keys past every row's position
+//    is replaced by 0 (such slots may hold anything, NaN included, and a
+//    masked key's probability 0 must not meet it).  K keeps ordinary loads:
+//    its fragments take a line in four pieces, four loads apart.
+//  * For each chunk row, a lane sums its 8 keys into its 8 dims; the four
+//    key groups are then added with two lane swaps that also split the dims
+//    (reduce-scatter: l ^ 32 keeps dims 0-3 or 4-7 of the slice, l ^ 16 two
+//    of those), so lane l ends with dims 8 (l % 16) + 4 (kg / 2) + 2 (kg % 2)
+//    and + 1, and the row's 128 outputs are one 512-byte store.
 __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel(PrefillAttnArgs a) {
   __shared__ __attribute__((aligned(16))) float s_p[kBlockWaves][kRowsPerChunk * kPStride];
   const AttnArgs& A = a.attn;
@@ -242,7 +250,8 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel
   const int p_n = A.q_start + t_n;
 
   float m_row = -INFINITY, l_row = 0.0f;
-  float vlo[kBlock], vhi[kBlock];  // V[k][2 lane], V[k][2 lane + 1]
+  const int kg = lane >> 4;  // key group of the lane's V rows
+  float vf[8][8];            // V[4 i + kg][8 (lane % 16) + d], fp32
   float* P = s_p[wave];
   if (ok) {
     const int64_t tile = ((int64_t)pb * A.heads + h) * (kBlock * kDim);
@@ -254,9 +263,9 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel
     bf16x8_t av[8], bq[8];
 #pragma unroll
     for (int st = 0; st < 8; ++st) av[st] = *reinterpret_cast<const bf16x8_t*>(kt + n * kDim + 16 * st + 8 * hh);
-    uint32_t vw[kBlock];
+    uint4 vw[8];
 #pragma unroll
-    for (int k = 0; k < kBlock; ++k) vw[k] = reinterpret_cast<const uint32_t*>(vt + k * kDim)[lane];
+    for (int i = 0; i < 8; ++i) vw[i] = load_stream16(reinterpret_cast<const uint4*>(vt) + i * kWave + lane);
 #pragma unroll
     for (int st = 0; st < 8; ++st) bq[st] = *reinterpret_cast<const bf16x8_t*>(qr + 16 * st + 8 * hh);
     f32x16_t c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[0], bq[0], f32x16_t{0}, 0, 0, 0);
@@ -290,10 +299,14 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel
 #pragma unroll
     for (int m_ = 1; m_ < kWave; m_ <<= 1) pmax = max(pmax, __shfl_xor(pmax, m_, kWave));
 #pragma unroll
-    for (int k = 0; k < kBlock; ++k) {
-      const bool seen = j * kBlock + k <= pmax;
-      vlo[k] = seen ? bf16_lo(vw[k]) : 0.0f;
-      vhi[k] = seen ? bf16_hi(vw[k]) : 0.0f;
+    for (int i = 0; i < 8; ++i) {
+      const bool seen = j * kBlock + 4 * i + kg <= pmax;
+      const uint32_t w4[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vf[i][2 * e] = seen ? bf16_lo(w4[e]) : 0.0f;
+        vf[i][2 * e + 1] = seen ? bf16_hi(w4[e]) : 0.0f;
+      }
     }
   }
   // (m, l) of chunk row n, written by its lane in the lower half.
@@ -307,22 +320,37 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel
     const int s_ = i - t * A.topk;
     float o0 = 0.0f, o1 = 0.0f;
     if (ok) {
+      float acc[8];
 #pragma unroll
-      for (int k4 = 0; k4 < kBlock / 4; ++k4) {
-        const float4 pr = *reinterpret_cast<const float4*>(P + r * kPStride + 4 * k4);
-        o0 += pr.x * vlo[4 * k4] + pr.y * vlo[4 * k4 + 1] + pr.z * vlo[4 * k4 + 2] + pr.w * vlo[4 * k4 + 3];
-        o1 += pr.x * vhi[4 * k4] + pr.y * vhi[4 * k4 + 1] + pr.z * vhi[4 * k4 + 2] + pr.w * vhi[4 * k4 + 3];
+      for (int d = 0; d < 8; ++d) acc[d] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pr = P[r * kPStride + 4 * i + kg];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[d] += pr * vf[i][d];
       }
+      float k1[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[d]), __float_as_uint(acc[4 + d]),
+                                                        false, false);
+        k1[d] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+      }
+      const auto y0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(k1[0]), __float_as_uint(k1[2]), false, false);
+      const auto y1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(k1[1]), __float_as_uint(k1[3]), false, false);
+      o0 = __uint_as_float(y0[0]) + __uint_as_float(y0[1]);
+      o1 = __uint_as_float(y1[0]) + __uint_as_float(y1[1]);
     }
     float* dst = w.part + (((int64_t)t * A.heads + h) * A.topk + s_) * kPartStride;
-    *reinterpret_cast<float2*>(dst + 2 * lane) = make_float2(o0, o1);
+    *reinterpret_cast<float2*>(dst + 8 * (lane & 15) + 4 * (kg >> 1) + 2 * (kg & 1)) = make_float2(o0, o1);
   }
 }
 
 // One wave per (row, head): log-sum-exp merge of the row's partials.  Lane s
 // (< 64) takes slot s's (m, l) and weight; then every slot's two output
-// values per lane are loaded together (weight 0 for slots that keep nothing)
-// and lane d produces dims d and d + 64.  No kept token gives out = 0,
+// values per lane are loaded together (weight 0 for slots that keep nothing;
+// non-temporal loads, each reading whole lines of a record read once) and
+// lane d produces dims d and d + 64.  No kept token gives out = 0,
 // lse = -inf.
 __global__ __launch_bounds__(kMergeWaves * kWave) void attn_prefill_merge_kernel(PrefillAttnArgs a) {
   const AttnArgs& A = a.attn;
@@ -365,8 +393,8 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void attn_prefill_merge_kernel
       for (int u = 0; u < 16; ++u) {
         fu[u] = u0 + u < ns ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(f), u0 + u)) : 0.0f;
         const float* ps = base + (int64_t)(s0 + u0 + u) * kPartStride;
-        o0[u] = fu[u] != 0.0f ? ps[lane] : 0.0f;
-        o1[u] = fu[u] != 0.0f ? ps[lane + kWave] : 0.0f;
+        o0[u] = fu[u] != 0.0f ? __builtin_nontemporal_load(ps + lane) : 0.0f;
+        o1[u] = fu[u] != 0.0f ? __builtin_nontemporal_load(ps + lane + kWave) : 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
