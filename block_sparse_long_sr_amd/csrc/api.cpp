@@ -233,6 +233,7 @@ static int attn_common(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint
       pa.attn = a;
       pa.ws = ws;
       pa.plan = P;
+      pa.plan.local_win = cfg->local_blocks > 0 ? cfg->local_blocks : 0;
       return hip_status(uocr::launch_attn_prefill_blocks(pa, static_cast<hipStream_t>(stream)), "sparse_attn_prefill");
     }
   }

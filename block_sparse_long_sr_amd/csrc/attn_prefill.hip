@@ -13,7 +13,10 @@
 // accumulation of exact bf16 products), takes the block's softmax per row
 // (max, exp2, sum: each lane owns 16 distinct scores of one row) and forms
 // P.V in fp32 (each lane two output dims over all 32 keys), writing the
-// row's partial state (m, l, o[128]) for the slot.  A merge pass combines
+// row's partial state (m, l, o[128]) for the slot.  The local window is
+// taken apart: a row's slots holding the window blocks of its own position
+// (shared by every row of a 32-row block) are attended per row block and
+// leave one partial per row instead of one per slot.  A merge pass combines
 // the partials of each (row, head) in log-sum-exp form.
 //
 // Slot rule, shared by the bucket and merge passes: slot s of row t holds
@@ -58,6 +61,39 @@ __device__ __forceinline__ bool slot_counts(int j, int p, int max_blocks) {
   return j >= 0 && j < max_blocks && j * kBlock <= p;
 }
 
+// Window slots: block j lies in the lw-block window ending at the block of
+// position p.  They are attended per row block by the local pass, not per
+// slot (a counting slot is either a window slot or a bucketed one).
+__device__ __forceinline__ bool in_window(int j, int p, int lw) {
+  const int bp = p >> 5;
+  return lw > 0 && j > bp - lw && j <= bp;
+}
+
+// Sum of a lane's 8 output dims over the wave's four key groups
+// (lanes l, l ^ 16, l ^ 32, l ^ 48), split over them: lanes l and l ^ 32
+// keep dims 0-3 or 4-7 of the slice, then lanes l and l ^ 16 two of those,
+// so lane l returns dims 8 (l % 16) + 4 (kg / 2) + 2 (kg % 2) and + 1
+// (kg = l / 16).  Each v_permlane*_swap of two registers leaves one
+// register's pair of values in the keeping lane (its own and its partner's).
+__device__ __forceinline__ void reduce_scatter_dims(const float (&acc)[8], float& d0, float& d1) {
+  float k1[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[d]), __float_as_uint(acc[4 + d]), false, false);
+    k1[d] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  }
+  const auto y0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(k1[0]), __float_as_uint(k1[2]), false, false);
+  const auto y1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(k1[1]), __float_as_uint(k1[3]), false, false);
+  d0 = __uint_as_float(y0[0]) + __uint_as_float(y0[1]);
+  d1 = __uint_as_float(y1[0]) + __uint_as_float(y1[1]);
+}
+
+// Row blocks of a chunk: runs of rows whose positions share one 32-token
+// block.
+__device__ __forceinline__ int row_blocks(const AttnArgs& A) {
+  return A.nq > 0 ? ((A.q_start + A.nq - 1) >> 5) - (A.q_start >> 5) + 1 : 0;
+}
+
 // i / d for 0 <= i < 2^31 and 1 <= d: the high product with floor((2^32-1)/d)
 // is floor(i/d) or one less; one correction step fixes it.
 __device__ __forceinline__ int div_by(int i, int d, uint32_t magic) {
@@ -80,7 +116,7 @@ __device__ __forceinline__ int div_by(int i, int d, uint32_t magic) {
 // rest in narrower rounds, once for the counts and again for the scatter.
 template <int N>
 __device__ __forceinline__ void bucket_round(const AttnArgs& A, int i0, int npairs, int topk, uint32_t magic, int M,
-                                             int (&jv)[N]) {
+                                             int lw, int (&jv)[N]) {
 #pragma unroll
   for (int u = 0; u < N; ++u) {
     const int i = i0 + u * kBucketThreads;
@@ -89,7 +125,8 @@ __device__ __forceinline__ void bucket_round(const AttnArgs& A, int i0, int npai
 #pragma unroll
   for (int u = 0; u < N; ++u) {
     const int i = i0 + u * kBucketThreads;
-    if (jv[u] >= 0 && !slot_counts(jv[u], A.q_start + div_by(i, topk, magic), M)) jv[u] = -1;
+    const int p = A.q_start + div_by(i, topk, magic);
+    if (jv[u] >= 0 && (!slot_counts(jv[u], p, M) || in_window(jv[u], p, lw))) jv[u] = -1;
   }
 }
 
@@ -116,7 +153,7 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
   const int npairs = A.nq * topk;
   const uint32_t magic = 0xFFFFFFFFu / (uint32_t)topk;
   int jf[kPairUnroll];  // the first round's blocks, kept for the scatter
-  bucket_round(A, tid, npairs, topk, magic, M, jf);
+  bucket_round(A, tid, npairs, topk, magic, M, a.plan.local_win, jf);
   for (int j = tid; j < M; j += kBucketThreads) s_cnt[j] = 0;
   __syncthreads();
   int rk[kPairUnroll];  // STAGE > 0: each pair's rank in its bucket
@@ -131,7 +168,7 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
   if constexpr (STAGE == 0) {
     for (int i0 = tid + kRound; i0 < npairs; i0 += kBucketThreads * kPairTail) {
       int jv[kPairTail];
-      bucket_round(A, i0, npairs, topk, magic, M, jv);
+      bucket_round(A, i0, npairs, topk, magic, M, a.plan.local_win, jv);
 #pragma unroll
       for (int u = 0; u < kPairTail; ++u)
         if (jv[u] >= 0) atomicAdd(&s_cnt[jv[u]], 1);
@@ -196,7 +233,7 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
       if (jf[u] >= 0) w.pairs[atomicAdd(&s_cnt[jf[u]], 1)] = tid + u * kBucketThreads;
     for (int i0 = tid + kRound; i0 < npairs; i0 += kBucketThreads * kPairTail) {
       int jv[kPairTail];
-      bucket_round(A, i0, npairs, topk, magic, M, jv);
+      bucket_round(A, i0, npairs, topk, magic, M, a.plan.local_win, jv);
 #pragma unroll
       for (int u = 0; u < kPairTail; ++u)
         if (jv[u] >= 0) w.pairs[atomicAdd(&s_cnt[jv[u]], 1)] = i0 + u * kBucketThreads;
@@ -329,21 +366,233 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel
 #pragma unroll
         for (int d = 0; d < 8; ++d) acc[d] += pr * vf[i][d];
       }
-      float k1[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[d]), __float_as_uint(acc[4 + d]),
-                                                        false, false);
-        k1[d] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-      }
-      const auto y0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(k1[0]), __float_as_uint(k1[2]), false, false);
-      const auto y1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(k1[1]), __float_as_uint(k1[3]), false, false);
-      o0 = __uint_as_float(y0[0]) + __uint_as_float(y0[1]);
-      o1 = __uint_as_float(y1[0]) + __uint_as_float(y1[1]);
+      reduce_scatter_dims(acc, o0, o1);
     }
     float* dst = w.part + (((int64_t)t * A.heads + h) * A.topk + s_) * kPartStride;
     *reinterpret_cast<float2*>(dst + 8 * (lane & 15) + 4 * (kg >> 1) + 2 * (kg & 1)) = make_float2(o0, o1);
   }
+}
+
+// The window slots of a row block in one pass.  Rows whose positions lie
+// in block bp share the window blocks bp - lw + 1 .. bp (lw = the local
+// window), which nearly every row keeps: one wave per (row block, head)
+// reads each window block's K and V tiles once and carries each row's
+// online-softmax state (m, l, o) over all of its window slots (a block a row
+// keeps c times counts c times; rows that do not keep it mask all of its
+// keys).  The state is written as one partial at the row's first window
+// slot; the bucket pass leaves window slots out and the merge reads only
+// that one, so the window adds no per-slot partials.
+//  * Scores: the block pass's MFMA layout (keys on M, rows on N); lane
+//    (n, hh) holds row n's scores of keys 8 (r / 4) + 4 hh + r % 4.
+//  * P.V on the matrix cores as well: O (rows x 128 dims, four 32-dim
+//    tiles) += P (rows x keys) V (keys x dims).  The A fragment of k-step st
+//    is the lane's own probabilities r = 8 st .. 8 st + 7 (k index 8 hh + e
+//    <-> key 4 hh + 16 st + 8 (e / 4) + e % 4, a summation-order permutation
+//    that B follows), split exactly into three bf16 terms (truncations of p
+//    and of the remainders: 8 + 8 + 8 mantissa bits), so the three products
+//    with the bf16 V are exact and summed in fp32.  B fragments are read
+//    from a transposed copy of the V tile in LDS (dims x keys; two 8-byte
+//    reads give a lane its 8 keys of one dim).  C register r of lane l holds
+//    row 8 (r / 4) + 4 hh + r % 4, dim l % 32 of the tile; the rescaling by
+//    each row's alpha reads the alphas from LDS.
+//  * V keys past every row's position are written to the copy as 0 (such
+//    slots may hold anything, NaN included).  K and V use ordinary loads: a
+//    window tile is shared by lw row blocks.
+constexpr int kVtStride = 36;  // keys per dim row of the transposed V copy (bf16), padded
+constexpr int kLocalIds = 16;  // block ids per row held in registers (topk <= 16, a multiple of 4)
+
+__device__ __forceinline__ bf16x8_t bf16x8_bits(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(bf16x8_t, make_uint4(a, b, c, d));
+}
+
+__global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_local_kernel(PrefillAttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[kBlockWaves][kDim * kVtStride];
+  __shared__ __attribute__((aligned(16))) float s_alpha[kBlockWaves][kRowsPerChunk];
+  __shared__ int32_t s_first[kBlockWaves][kRowsPerChunk];
+  const AttnArgs& A = a.attn;
+  const WsView w = ws_view(a);
+  const int wave = wave_id();
+  const int lw = a.plan.local_win;
+  const int64_t unit = (int64_t)blockIdx.x * kBlockWaves + wave;
+  const int rb = (int)(unit / A.heads);
+  const int h = (int)(unit - (int64_t)rb * A.heads);
+  if (rb >= row_blocks(A)) return;
+  const int bp = (A.q_start >> 5) + rb;
+  const int t0 = max(0, bp * kBlock - A.q_start);
+  const int nrows = min(A.nq, (bp + 1) * kBlock - A.q_start) - t0;  // 1 .. 32
+  const int lane = lane_id();
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int kg = lane >> 4;
+  const bool row_ok = n < nrows;
+  const int t_n = t0 + (row_ok ? n : 0);
+  const int p_n = A.q_start + t_n;
+  const int32_t* ids = A.block_idx + (int64_t)t_n * A.topk;
+  // up to 16 block ids of the row in registers (one 16-byte load per 4), so
+  // the window bookkeeping below reads memory once
+  const bool reg_ids = A.topk <= kLocalIds && (A.topk & 3) == 0 && (reinterpret_cast<uintptr_t>(A.block_idx) & 15) == 0;
+  int idr[kLocalIds];
+#pragma unroll
+  for (int k4 = 0; k4 < kLocalIds / 4; ++k4) {
+    int4 v = make_int4(-1, -1, -1, -1);
+    if (reg_ids && 4 * k4 < A.topk) v = *reinterpret_cast<const int4*>(ids + 4 * k4);
+    idr[4 * k4] = v.x;
+    idr[4 * k4 + 1] = v.y;
+    idr[4 * k4 + 2] = v.z;
+    idr[4 * k4 + 3] = v.w;
+  }
+  // the row's first window slot: where its partial goes (-1: none)
+  int sf = -1;
+  if (reg_ids) {
+#pragma unroll
+    for (int s_ = kLocalIds - 1; s_ >= 0; --s_)
+      if (slot_counts(idr[s_], p_n, A.max_blocks) && in_window(idr[s_], p_n, lw)) sf = s_;
+  } else {
+    for (int s_ = A.topk - 1; s_ >= 0; --s_) {
+      const int j = ids[s_];
+      if (slot_counts(j, p_n, A.max_blocks) && in_window(j, p_n, lw)) sf = s_;
+    }
+  }
+  if (!row_ok) sf = -1;
+  if (__ballot(sf >= 0) == 0) return;
+  if (hh == 0) s_first[wave][n] = sf;
+  const uint16_t* qr = A.q + ((int64_t)t_n * A.heads + h) * kDim;
+  bf16x8_t bq[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) bq[st] = *reinterpret_cast<const bf16x8_t*>(qr + 16 * st + 8 * hh);
+  const int pmax = A.q_start + t0 + nrows - 1;  // keys past it are masked for every row
+  uint16_t* vt_l = s_vt[wave];
+
+  float m_row = -INFINITY, l_row = 0.0f;
+  f32x16_t acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16_t{0};
+  // Window blocks one at a time.  A block no row keeps, outside the table
+  // or with an out-of-range pool index is skipped: it changes nothing.
+  for (int jj = 0; jj < lw; ++jj) {
+    {
+      const int j = bp - lw + 1 + jj;
+      if (j < 0 || j >= A.max_blocks) continue;
+      int c = 0;  // how many of row n's slots keep block j
+      if (row_ok) {
+        if (reg_ids) {
+#pragma unroll
+          for (int s_ = 0; s_ < kLocalIds; ++s_) c += idr[s_] == j ? 1 : 0;
+        } else {
+          for (int s_ = 0; s_ < A.topk; ++s_) c += ids[s_] == j ? 1 : 0;
+        }
+      }
+      if (__ballot(c > 0) == 0) continue;
+      const int pb = __builtin_amdgcn_readfirstlane(A.block_table[j]);  // sequence 0
+      if (pb < 0 || (int64_t)pb >= A.num_blocks) continue;
+      const int64_t tile = ((int64_t)pb * A.heads + h) * (kBlock * kDim);
+      const uint16_t* kt = A.k_pool + tile;
+      const uint16_t* vt = A.v_pool + tile;
+      bf16x8_t av[8];
+#pragma unroll
+      for (int st = 0; st < 8; ++st) av[st] = *reinterpret_cast<const bf16x8_t*>(kt + n * kDim + 16 * st + 8 * hh);
+      uint4 vw[8];  // V[4 i + kg][8 (lane % 16) .. +8]
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vw[i] = reinterpret_cast<const uint4*>(vt)[i * kWave + lane];
+      f32x16_t cc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[0], bq[0], f32x16_t{0}, 0, 0, 0);
+#pragma unroll
+      for (int st = 1; st < 8; ++st) cc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[st], bq[st], cc, 0, 0, 0);
+
+      const int key0 = j * kBlock + 4 * hh;
+      float z[16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + (r & 3);
+        z[r] = (c > 0 && key <= p_n) ? cc[r] * A.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, z[r]);
+      }
+      const float m_new = fmaxf(m_row, max_xor32(mx));
+      // 1 when the max does not move (also for rows that saw no key yet)
+      const float alpha = m_new == m_row ? 1.0f : exp2f(m_row - m_new);
+      const float cf = (float)c;
+      float sum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        z[r] = z[r] == -INFINITY ? 0.0f : cf * exp2f(z[r] - m_new);
+        sum += z[r];
+      }
+      l_row = l_row * alpha + sum_xor32(sum);
+      m_row = m_new;
+      if (hh == 0) s_alpha[wave][n] = alpha;
+      // transposed V copy: vt_l[dim * kVtStride + key]
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int key = 4 * i + kg;
+        const bool seen = j * kBlock + key <= pmax;
+        const uint32_t w4[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int dim = 8 * (lane & 15) + 2 * e;
+          vt_l[dim * kVtStride + key] = seen ? (uint16_t)(w4[e] & 0xFFFFu) : (uint16_t)0;
+          vt_l[(dim + 1) * kVtStride + key] = seen ? (uint16_t)(w4[e] >> 16) : (uint16_t)0;
+        }
+      }
+      // rescale O by each row's alpha (rows 8 q + 4 hh + 0..3 of the C layout)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 al = *reinterpret_cast<const float4*>(&s_alpha[wave][8 * q + 4 * hh]);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          acc[dt][4 * q] *= al.x;
+          acc[dt][4 * q + 1] *= al.y;
+          acc[dt][4 * q + 2] *= al.z;
+          acc[dt][4 * q + 3] *= al.w;
+        }
+      }
+      // exact three-term bf16 split of P, A fragments of k-steps 0 and 1
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        uint32_t t1[8], t2[8], t3[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = z[8 * st + e];
+          const uint32_t b1 = __float_as_uint(pv) & 0xFFFF0000u;
+          const float r1 = pv - __uint_as_float(b1);
+          const uint32_t b2 = __float_as_uint(r1) & 0xFFFF0000u;
+          const float r2 = r1 - __uint_as_float(b2);
+          t1[e] = b1 >> 16;
+          t2[e] = b2 >> 16;
+          t3[e] = __float_as_uint(r2) >> 16;
+        }
+        const bf16x8_t a1 = bf16x8_bits(t1[0] | t1[1] << 16, t1[2] | t1[3] << 16, t1[4] | t1[5] << 16, t1[6] | t1[7] << 16);
+        const bf16x8_t a2 = bf16x8_bits(t2[0] | t2[1] << 16, t2[2] | t2[3] << 16, t2[4] | t2[5] << 16, t2[6] | t2[7] << 16);
+        const bf16x8_t a3 = bf16x8_bits(t3[0] | t3[1] << 16, t3[2] | t3[3] << 16, t3[4] | t3[5] << 16, t3[6] | t3[7] << 16);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const uint16_t* src = vt_l + (32 * dt + n) * kVtStride + 4 * hh + 16 * st;
+          const uint2 lo = *reinterpret_cast<const uint2*>(src);
+          const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+          const bf16x8_t bv = bf16x8_bits(lo.x, lo.y, hi.x, hi.y);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bv, acc[dt], 0, 0, 0);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, bv, acc[dt], 0, 0, 0);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, bv, acc[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // partial of each row with a window slot: row 8 q + 4 hh + u, dim 32 dt + n
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = 8 * q + 4 * hh + u;
+      if (r < nrows) {
+        const int sr = s_first[wave][r];
+        if (sr >= 0) {
+          float* dst = w.part + (((int64_t)(t0 + r) * A.heads + h) * A.topk + sr) * kPartStride + n;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) dst[32 * dt] = acc[dt][4 * q + u];
+        }
+      }
+    }
+  }
+  if (hh == 0 && sf >= 0) w.ml[((int64_t)t_n * A.heads + h) * A.topk + sf] = make_float2(m_row, l_row);
 }
 
 // One wave per (row, head): log-sum-exp merge of the row's partials.  Lane s
@@ -364,10 +613,23 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void attn_prefill_merge_kernel
   const float* base = w.part + (int64_t)item * A.topk * kPartStride;
   const float2* mls = w.ml + (int64_t)item * A.topk;
 
+  // the row's first window slot holds the partial of all its window slots
+  const int lw = a.plan.local_win;
+  int sfirst = -1;
+  for (int s0 = 0; lw > 0 && s0 < A.topk; s0 += kWave) {
+    const int s = s0 + lane;
+    const int j = s < A.topk ? sel[s] : -1;
+    const uint64_t win = __ballot(s < A.topk && slot_counts(j, p, A.max_blocks) && in_window(j, p, lw));
+    if (win != 0) {
+      sfirst = s0 + __builtin_ctzll(win);
+      break;
+    }
+  }
   float res0 = 0.0f, res1 = 0.0f, L = 0.0f, M = -INFINITY;
   for (int s0 = 0; s0 < A.topk; s0 += kWave) {  // one round for topk <= 64
     const int s = s0 + lane;
-    const bool valid = s < A.topk && slot_counts(sel[s], p, A.max_blocks);
+    const int js = s < A.topk ? sel[s] : -1;
+    const bool valid = s < A.topk && slot_counts(js, p, A.max_blocks) && (!in_window(js, p, lw) || s == sfirst);
     float2 ml = make_float2(-INFINITY, 0.0f);
     if (valid) ml = mls[s];
     float Mr = ml.x;
@@ -440,6 +702,12 @@ PrefillAttnPlan prefill_attn_plan(int32_t T, int32_t heads, int32_t topk, int32_
   return p;
 }
 
+namespace {
+int row_blocks_host(const AttnArgs& A) {
+  return A.nq > 0 ? ((A.q_start + A.nq - 1) >> 5) - (A.q_start >> 5) + 1 : 0;
+}
+}  // namespace
+
 hipError_t launch_attn_prefill_blocks(const PrefillAttnArgs& a, hipStream_t stream) {
   const AttnArgs& A = a.attn;
   if (A.nq == 0) return hipSuccess;
@@ -450,6 +718,12 @@ hipError_t launch_attn_prefill_blocks(const PrefillAttnArgs& a, hipStream_t stre
   else
     hipLaunchKernelGGL((attn_prefill_bucket_kernel<kMaxBlocksAttnBucket, 0>), dim3(1), dim3(kBucketThreads), 0,
                        stream, a);
+  if (a.plan.local_win > 0) {
+    const int64_t lunits = (int64_t)row_blocks_host(A) * A.heads;
+    if (lunits > 0)
+      hipLaunchKernelGGL(attn_prefill_local_kernel, dim3((unsigned)((lunits + kBlockWaves - 1) / kBlockWaves)),
+                         dim3(kBlockWaves * kWave), 0, stream, a);
+  }
   const int64_t units = (int64_t)a.plan.max_chunks * A.heads;
   hipLaunchKernelGGL(attn_prefill_block_kernel, dim3((unsigned)((units + kBlockWaves - 1) / kBlockWaves)),
                      dim3(kBlockWaves * kWave), 0, stream, a);
