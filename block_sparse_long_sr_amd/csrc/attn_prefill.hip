@@ -23,6 +23,8 @@
 // block j = block_idx[t][s]; it contributes iff 0 <= j < max_blocks and
 // 32 j <= p (p = q_start + t).  A block whose pool index is out of range
 // contributes nothing (partial m = -inf, l = 0).
+#include <mutex>
+
 #include "attn_common.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -706,11 +708,56 @@ namespace {
 int row_blocks_host(const AttnArgs& A) {
   return A.nq > 0 ? ((A.q_start + A.nq - 1) >> 5) - (A.q_start >> 5) + 1 : 0;
 }
+
+// The window pass does not depend on the bucketing, and the bucketing runs
+// in one workgroup, so the window pass runs beside it on a second stream
+// (default priority, non-blocking), forked from and joined back to the
+// caller's stream with two events: one stream and two events per device,
+// created on first use and held until the process ends.  A mutex per device
+// keeps each call's fork, launch and join together.  If they cannot be
+// created, the window pass runs on the caller's stream.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipError_t status = hipSuccess;
+  std::mutex mu;
+};
+constexpr int kMaxDevices = 64;
+std::once_flag g_side_once[kMaxDevices];
+SideStream g_side[kMaxDevices];
+
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_side_once[dev], [dev] {
+    SideStream& s = g_side[dev];
+    s.status = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking);
+    if (s.status == hipSuccess) s.status = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming);
+    if (s.status == hipSuccess) s.status = hipEventCreateWithFlags(&s.join, hipEventDisableTiming);
+  });
+  return g_side[dev].status == hipSuccess ? &g_side[dev] : nullptr;
+}
 }  // namespace
 
 hipError_t launch_attn_prefill_blocks(const PrefillAttnArgs& a, hipStream_t stream) {
   const AttnArgs& A = a.attn;
   if (A.nq == 0) return hipSuccess;
+  const int64_t lunits = a.plan.local_win > 0 ? (int64_t)row_blocks_host(A) * A.heads : 0;
+  const dim3 lgrid((unsigned)((lunits + kBlockWaves - 1) / kBlockWaves));
+  SideStream* side = lunits > 0 ? side_stream() : nullptr;
+  std::unique_lock<std::mutex> lock;
+  if (side != nullptr) {
+    lock = std::unique_lock<std::mutex>(side->mu);
+    hipError_t e = hipEventRecord(side->fork, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_prefill_local_kernel, lgrid, dim3(kBlockWaves * kWave), 0, side->stream, a);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipEventRecord(side->join, side->stream);
+    if (e != hipSuccess) return e;
+  } else if (lunits > 0) {
+    hipLaunchKernelGGL(attn_prefill_local_kernel, lgrid, dim3(kBlockWaves * kWave), 0, stream, a);
+  }
   // Staged bucketing: counts for up to 4096 blocks (16 KB) and up to 32768
   // pairs (128 KB) in LDS, beside the 8 KB scan.
   if (A.max_blocks <= 4096 && (int64_t)A.nq * A.topk <= 32768)
@@ -718,15 +765,13 @@ hipError_t launch_attn_prefill_blocks(const PrefillAttnArgs& a, hipStream_t stre
   else
     hipLaunchKernelGGL((attn_prefill_bucket_kernel<kMaxBlocksAttnBucket, 0>), dim3(1), dim3(kBucketThreads), 0,
                        stream, a);
-  if (a.plan.local_win > 0) {
-    const int64_t lunits = (int64_t)row_blocks_host(A) * A.heads;
-    if (lunits > 0)
-      hipLaunchKernelGGL(attn_prefill_local_kernel, dim3((unsigned)((lunits + kBlockWaves - 1) / kBlockWaves)),
-                         dim3(kBlockWaves * kWave), 0, stream, a);
-  }
   const int64_t units = (int64_t)a.plan.max_chunks * A.heads;
   hipLaunchKernelGGL(attn_prefill_block_kernel, dim3((unsigned)((units + kBlockWaves - 1) / kBlockWaves)),
                      dim3(kBlockWaves * kWave), 0, stream, a);
+  if (side != nullptr) {  // the merge reads the window partials
+    const hipError_t e = hipStreamWaitEvent(stream, side->join, 0);
+    if (e != hipSuccess) return e;
+  }
   const int64_t items = (int64_t)A.nq * A.heads;
   hipLaunchKernelGGL(attn_prefill_merge_kernel, dim3((unsigned)((items + kMergeWaves - 1) / kMergeWaves)),
                      dim3(kMergeWaves * kWave), 0, stream, a);

@@ -355,6 +355,13 @@ int uocr_block_topk_prefill(const uocr_sparse_cfg* cfg, const void* cand_ws, siz
  *         does not apply (max_blocks > 16384), and the row-major path then runs
  *         whatever ws is.  UOCR_EWORKSPACE: ws non-NULL and too small;
  *         UOCR_EINVAL: ws not 256-byte aligned.
+ *         The block-major path attends each 32-row block's local-window blocks
+ *         in a pass of its own, which it runs on a second stream of the
+ *         library's (one per device, default priority, created with two events
+ *         on the first such call and kept until the process ends): forked from
+ *         `stream` with an event and joined back before the merge, so the call
+ *         stays ordered on `stream` and can be captured in a HIP graph.  If the
+ *         stream or events cannot be created, that pass runs on `stream`.
  */
 int uocr_sparse_attn_prefill(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const uint16_t* q, int32_t q_start,
                              int32_t T, const int32_t* block_idx, float* out, float* lse, void* ws,

@@ -215,3 +215,53 @@ def test_prefill_attention_block_major_matches_row_major_and_oracle():
         k_, v_ = G.fetcher(wl, 0, 0)(toks)
         o2, l2 = oracle.attend(q[t], k_, v_, np.arange(toks.size), cfg_o.sm_scale)
         G.check_attention(res_b["out"][t], res_b["lse"][t], o2, l2)
+
+
+def test_prefill_attention_graph_capture_and_concurrent_streams():
+    """The block-major prefill attention forks its window pass onto a second
+    stream and joins it back: captured in a HIP graph and replayed with eager
+    work in between, and called on two streams at once with their own
+    workspaces, it gives the eager results bit for bit."""
+    wl = W.prefill_case("prefill attention graph S=9000 q_start=7000 T=1500", 0xFA, 9000, 7000, 1500)
+    print("case:", wl.name, flush=True)
+    cfg = G.cfg_for(wl)
+    dev = SD.generate(wl)
+    ref = G.gpu_prefill(dev, cfg)
+    T, M, H, D = wl.rows, wl.max_blocks, wl.heads, wl.head_dim
+    kv = dev.kv(0)
+    idx = torch.from_numpy(ref["idx"]).cuda()
+    ab = U.workspace_size(cfg, U.OP_ATTN_PREFILL, T, M)
+    aws = torch.zeros(ab, dtype=torch.uint8, device="cuda")
+    out = torch.zeros((T, H, D), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((T, H), dtype=torch.float32, device="cuda")
+    cap = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cap):
+        U.sparse_attn_prefill(cfg, kv, dev.q, wl.q_start, T, idx, out, lse, ws=aws, stream=cap.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        aws.fill_(0xA5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref["out"].view(np.uint32))
+        np.testing.assert_array_equal(lse.cpu().numpy().view(np.uint32), ref["lse"].view(np.uint32))
+        G.gpu_prefill(dev, cfg)  # eager work between replays
+    # two calls at once on two streams, each with its own workspace and outputs
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    aws2 = torch.zeros(ab, dtype=torch.uint8, device="cuda")
+    out2 = torch.full((T, H, D), float("nan"), dtype=torch.float32, device="cuda")
+    lse2 = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    out.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    torch.cuda.synchronize()
+    for _ in range(3):
+        U.sparse_attn_prefill(cfg, kv, dev.q, wl.q_start, T, idx, out, lse, ws=aws, stream=s1.cuda_stream)
+        U.sparse_attn_prefill(cfg, kv, dev.q, wl.q_start, T, idx, out2, lse2, ws=aws2, stream=s2.cuda_stream)
+    torch.cuda.synchronize()
+    for o, l in ((out, lse), (out2, lse2)):
+        np.testing.assert_array_equal(o.cpu().numpy().view(np.uint32), ref["out"].view(np.uint32))
+        np.testing.assert_array_equal(l.cpu().numpy().view(np.uint32), ref["lse"].view(np.uint32))
