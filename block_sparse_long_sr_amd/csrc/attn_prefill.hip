@@ -246,9 +246,12 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
 // One wave per (chunk, head).  Lane l works on chunk row n = l % 32 and
 // half hh = l / 32 for the scores.
 //  * A fragment of step s (dims 16 s + 8 hh .. +8, the summation-order
-//    permutation shared by A and B, so the two lanes of a row read 32
-//    adjacent bytes): K row n; B fragment: q of chunk row n
-//    (rows past the chunk repeat row 0; their results are never used).
+//    permutation shared by A and B): K row n, read from a wave-private LDS
+//    copy of the tile; B fragment: q of chunk row n (rows past the chunk
+//    repeat row 0; their results are never used).  The K tile reaches LDS
+//    through eight 1 KB-contiguous non-temporal loads (like V below), its
+//    16-byte chunk c of row r stored at c ^ (r % 16) so that neither the
+//    copy nor the fragment reads of 32 rows at one column conflict in banks.
 //  * C register r of lane l holds the score of key 8 (r / 4) + 4 hh + r % 4
 //    for chunk row n.
 //  * P goes through a wave-private LDS tile [32 rows][kPStride].
@@ -257,8 +260,7 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
 //    caches): lane l holds dims 8 (l % 16) .. +8 of keys 4 i + kg, i = 0..7,
 //    kg = l / 16, widened to fp32 once.  V of keys past every row's position
 //    is replaced by 0 (such slots may hold anything, NaN included, and a
-//    masked key's probability 0 must not meet it).  K keeps ordinary loads:
-//    its fragments take a line in four pieces, four loads apart.
+//    masked key's probability 0 must not meet it).
 //  * For each chunk row, a lane sums its 8 keys into its 8 dims; the four
 //    key groups are then added with two lane swaps that also split the dims
 //    (reduce-scatter: l ^ 32 keeps dims 0-3 or 4-7 of the slice, l ^ 16 two
@@ -266,6 +268,7 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
 //    and + 1, and the row's 128 outputs are one 512-byte store.
 __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel(PrefillAttnArgs a) {
   __shared__ __attribute__((aligned(16))) float s_p[kBlockWaves][kRowsPerChunk * kPStride];
+  __shared__ __attribute__((aligned(16))) uint4 s_k[kBlockWaves][kBlock * 16];  // K tile, 16-byte chunk c of row r at c ^ (r % 16)
   const AttnArgs& A = a.attn;
   const WsView w = ws_view(a);
   const int wave = wave_id();
@@ -300,13 +303,23 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel
     // K and V depend only on the descriptor: issued first, while this
     // lane's pair (and with it the row of q) is still in flight
     bf16x8_t av[8], bq[8];
+    uint4 kw[8];  // row 4 i + lane / 16, chunk lane % 16
 #pragma unroll
-    for (int st = 0; st < 8; ++st) av[st] = *reinterpret_cast<const bf16x8_t*>(kt + n * kDim + 16 * st + 8 * hh);
+    for (int i = 0; i < 8; ++i) kw[i] = load_stream16(reinterpret_cast<const uint4*>(kt) + i * kWave + lane);
     uint4 vw[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) vw[i] = load_stream16(reinterpret_cast<const uint4*>(vt) + i * kWave + lane);
 #pragma unroll
     for (int st = 0; st < 8; ++st) bq[st] = *reinterpret_cast<const bf16x8_t*>(qr + 16 * st + 8 * hh);
+    uint4* K = s_k[wave];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      K[r * 16 + ((lane & 15) ^ (r & 15))] = kw[i];
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+      av[st] = __builtin_bit_cast(bf16x8_t, K[n * 16 + ((2 * st + hh) ^ (n & 15))]);
     f32x16_t c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[0], bq[0], f32x16_t{0}, 0, 0, 0);
 #pragma unroll
     for (int st = 1; st < 8; ++st) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[st], bq[st], c, 0, 0, 0);
