@@ -267,8 +267,10 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
 //    of those), so lane l ends with dims 8 (l % 16) + 4 (kg / 2) + 2 (kg % 2)
 //    and + 1, and the row's 128 outputs are one 512-byte store.
 __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel(PrefillAttnArgs a) {
-  __shared__ __attribute__((aligned(16))) float s_p[kBlockWaves][kRowsPerChunk * kPStride];
-  __shared__ __attribute__((aligned(16))) uint4 s_k[kBlockWaves][kBlock * 16];  // K tile, 16-byte chunk c of row r at c ^ (r % 16)
+  // per wave: the K tile (16-byte chunk c of row r at c ^ (r % 16)), then,
+  // once the fragments are in registers, the P tile in the same bytes
+  __shared__ __attribute__((aligned(16))) uint4 s_k[kBlockWaves][kBlock * 16];
+  static_assert(kRowsPerChunk * kPStride * 4 <= kBlock * 16 * 16, "P fits in the K tile's bytes");
   const AttnArgs& A = a.attn;
   const WsView w = ws_view(a);
   const int wave = wave_id();
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel
   float m_row = -INFINITY, l_row = 0.0f;
   const int kg = lane >> 4;  // key group of the lane's V rows
   float vf[8][8];            // V[4 i + kg][8 (lane % 16) + d], fp32
-  float* P = s_p[wave];
+  float* P = reinterpret_cast<float*>(s_k[wave]);
   if (ok) {
     const int64_t tile = ((int64_t)pb * A.heads + h) * (kBlock * kDim);
     const uint16_t* kt = A.k_pool + tile;
