@@ -142,7 +142,7 @@ template <int CNT, int STAGE>
 __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(PrefillAttnArgs a) {
   static_assert(STAGE <= kBucketThreads * kPairUnroll, "staged pairs must all be in the first round");
   __shared__ int32_t s_cnt[CNT];
-  __shared__ int32_t s_scan[2][kBucketThreads];
+  __shared__ int32_t s_wsum[2][kBucketThreads / kWave];  // per-wave sums of the two scans
   __shared__ int32_t s_stage[STAGE > 0 ? STAGE : 1];
   const AttnArgs& A = a.attn;
   const WsView w = ws_view(a);
@@ -186,18 +186,33 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
     sp += c;
     sc += (c + kRowsPerChunk - 1) / kRowsPerChunk;
   }
-  s_scan[0][tid] = sp;
-  s_scan[1][tid] = sc;
-  __syncthreads();
-  for (int d = 1; d < kBucketThreads; d <<= 1) {  // inclusive scan of both sums
-    const int x0 = tid >= d ? s_scan[0][tid - d] : 0;
-    const int x1 = tid >= d ? s_scan[1][tid - d] : 0;
-    __syncthreads();
-    s_scan[0][tid] += x0;
-    s_scan[1][tid] += x1;
-    __syncthreads();
+  // exclusive scans of both sums: within each wave by lane shifts, then over
+  // the 16 wave sums (one barrier instead of two per doubling step)
+  const int lane = tid & (kWave - 1), wv = tid / kWave;
+  int ip = sp, ic = sc;
+#pragma unroll 1
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int xp = __shfl_up(ip, d, kWave), xc = __shfl_up(ic, d, kWave);
+    if (lane >= d) {
+      ip += xp;
+      ic += xc;
+    }
   }
-  int po = s_scan[0][tid] - sp, co = s_scan[1][tid] - sc;
+  if (lane == kWave - 1) {
+    s_wsum[0][wv] = ip;
+    s_wsum[1][wv] = ic;
+  }
+  __syncthreads();
+  int tot_p = 0, tot_c = 0, before_p = 0, before_c = 0;
+#pragma unroll 1
+  for (int w_ = 0; w_ < kBucketThreads / kWave; ++w_) {  // not unrolled: the pairs held in registers leave no room
+    const int x0 = s_wsum[0][w_], x1 = s_wsum[1][w_];
+    before_p += w_ < wv ? x0 : 0;
+    before_c += w_ < wv ? x1 : 0;
+    tot_p += x0;
+    tot_c += x1;
+  }
+  int po = before_p + ip - sp, co = before_c + ic - sc;
   for (int j = j0; j < j1; ++j) {
     const int c = s_cnt[j];
     const int nch = (c + kRowsPerChunk - 1) / kRowsPerChunk;
@@ -213,11 +228,11 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
     co += nch;
   }
   if (tid == kBucketThreads - 1) {
-    w.off[M] = s_scan[0][kBucketThreads - 1];
-    w.choff[M] = s_scan[1][kBucketThreads - 1];
+    w.off[M] = tot_p;
+    w.choff[M] = tot_c;
   }
   // descriptors past the last chunk: none
-  for (int g = s_scan[1][kBucketThreads - 1] + tid; g < a.plan.max_chunks; g += kBucketThreads)
+  for (int g = tot_c + tid; g < a.plan.max_chunks; g += kBucketThreads)
     w.desc[g] = make_int4(-1, 0, 0, -1);
   __syncthreads();
   if constexpr (STAGE > 0) {
@@ -227,7 +242,7 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
     for (int u = 0; u < kPairUnroll; ++u)
       if (jf[u] >= 0) s_stage[s_cnt[jf[u]] + rk[u]] = tid + u * kBucketThreads;
     __syncthreads();
-    const int total = s_scan[0][kBucketThreads - 1];
+    const int total = tot_p;
     for (int k = tid; k < total; k += kBucketThreads) w.pairs[k] = s_stage[k];
   } else {
 #pragma unroll
