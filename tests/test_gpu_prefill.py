@@ -68,8 +68,11 @@ def test_prefill_small_integer_inputs_exact():
     check_prefill(wl, range(wl.rows), exact=True)
 
 
-@pytest.mark.parametrize("topk,local", [(8, 2), (20, 4), (5, 4), (4, 4)])
+@pytest.mark.parametrize("topk,local", [(8, 2), (20, 4), (5, 4), (4, 4), (16, 1), (24, 8)])
 def test_prefill_remote_slot_variants(topk, local):
+    """Selection sizes and local windows: topk above 16 or not a multiple of 4
+    takes the window pass's general path for the row's block ids; local 1
+    and 8 change the window the pass covers per 32-row block."""
     wl = W.prefill_case(f"prefill topk {topk} local {local}", 0xF4 + topk, 2500, 2200, 300)
     print("case:", wl.name, flush=True)
     check_prefill(wl, range(0, wl.rows, 3), topk, local)
