@@ -413,6 +413,18 @@ def run_prefill(U, SD, W, torch, iters=5):
     # phase timed inside the step with an event pair around it (which adds
     # the phase's launch latency to it).
     t_step = loop((scoring, merge, attention), 4 * iters)
+    # the same step captured once in a HIP graph and replayed back to back
+    # (the window pass's fork and join are captured with it)
+    cap = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cap):
+        U.indexer_score_prefill(cfg, kv, dev.q_idx, wl.q_start, T, wsarg, stream=cap.cuda_stream)
+        U.block_topk_prefill(cfg, wsarg, wl.q_start, T, M, idx, stream=cap.cuda_stream)
+        U.sparse_attn_prefill(cfg, kv, dev.q, wl.q_start, T, idx, out, lse, ws=aws, stream=cap.cuda_stream)
+    torch.cuda.synchronize()
+    t_graph = loop((graph.replay,), 4 * iters)
+    del graph
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters + 2)]
     for i in range(iters + 2):
         e = ev[i]
@@ -450,9 +462,11 @@ def run_prefill(U, SD, W, torch, iters=5):
         "workload": wl.name,
         "rows": T,
         "tokens_per_s": T / (t_step * 1e-3),
-        "ms": {"step": t_step, "scoring": t_sc, "merge": t_mg, "attention": t_at, "scoring_back_to_back": t_sc_alone},
-        "ms_note": "step: back-to-back chunk steps, one event pair around them; scoring/merge/attention: one event "
-                   "pair around each phase inside the step (its launch latency included)",
+        "ms": {"step": t_step, "step_graph": t_graph, "scoring": t_sc, "merge": t_mg, "attention": t_at,
+               "scoring_back_to_back": t_sc_alone},
+        "ms_note": "step: back-to-back chunk steps, one event pair around them; step_graph: the same with the step "
+                   "captured in a HIP graph and replayed; scoring/merge/attention: one event pair around each phase "
+                   "inside the step (its launch latency included)",
         "scoring_back_to_back_batches_ms": batches,
         "scoring_in_step_TFLOPs": flops / (t_sc * 1e-3) / 1e12,
         # frac: the kernel in steady state (back-to-back batches above);
@@ -1004,7 +1018,7 @@ def main():
         log("chunked prefill T=2048 at 129024 of 131072")
         result["prefill"] = run_prefill(U, SD, W, torch)
         pf = result["prefill"]
-        log(f"prefill chunk step {pf['ms']['step'] * 1e3:.1f} us; scoring {pf['ms']['scoring_back_to_back'] * 1e3:.1f} us "
+        log(f"prefill chunk step {pf['ms']['step'] * 1e3:.1f} us ({pf['ms']['step_graph'] * 1e3:.1f} us as a HIP graph); scoring {pf['ms']['scoring_back_to_back'] * 1e3:.1f} us "
             f"back to back ({pf['scoring_roofline']['achieved']:.0f} TFLOP/s), {pf['ms']['scoring'] * 1e3:.1f} us in the "
             f"step; merge {pf['ms']['merge'] * 1e3:.1f} us; attention {pf['ms']['attention'] * 1e3:.1f} us")
 
