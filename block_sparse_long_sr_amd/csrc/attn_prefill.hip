@@ -154,6 +154,14 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
   // same-block LDS atomics within a wave to a few lanes.
   const int npairs = A.nq * topk;
   const uint32_t magic = 0xFFFFFFFFu / (uint32_t)topk;
+  // the pool indices of this thread's blocks (for the descriptors), read
+  // now so that the load overlaps the pair loads and the counting
+  constexpr int kSeg = (CNT + kBucketThreads - 1) / kBucketThreads;
+  const int seg = (M + kBucketThreads - 1) / kBucketThreads;  // <= kSeg
+  const int j0 = min(tid * seg, M), j1 = min(j0 + seg, M);
+  int pbs[kSeg];
+#pragma unroll
+  for (int k = 0; k < kSeg; ++k) pbs[k] = j0 + k < j1 ? A.block_table[j0 + k] : -1;  // sequence 0
   int jf[kPairUnroll];  // the first round's blocks, kept for the scatter
   bucket_round(A, tid, npairs, topk, magic, M, a.plan.local_win, jf);
   for (int j = tid; j < M; j += kBucketThreads) s_cnt[j] = 0;
@@ -178,8 +186,6 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
   }
   __syncthreads();
 
-  const int seg = (M + kBucketThreads - 1) / kBucketThreads;
-  const int j0 = min(tid * seg, M), j1 = min(j0 + seg, M);
   int sp = 0, sc = 0;
   for (int j = j0; j < j1; ++j) {
     const int c = s_cnt[j];
@@ -213,13 +219,16 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
     tot_c += x1;
   }
   int po = before_p + ip - sp, co = before_c + ic - sc;
-  for (int j = j0; j < j1; ++j) {
+#pragma unroll
+  for (int k = 0; k < kSeg; ++k) {
+    const int j = j0 + k;
+    if (j >= j1) break;
     const int c = s_cnt[j];
     const int nch = (c + kRowsPerChunk - 1) / kRowsPerChunk;
     w.off[j] = po;
     w.choff[j] = co;
     if (nch > 0) {
-      const int pb = A.block_table[j];  // sequence 0
+      const int pb = pbs[k];
       for (int q = 0; q < nch; ++q)
         w.desc[co + q] = make_int4(j, po + q * kRowsPerChunk, min(kRowsPerChunk, c - q * kRowsPerChunk), pb);
     }
