@@ -123,11 +123,11 @@ def test_decode_on_caches_written_by_the_rope_kernel():
 
 def test_page_coords_prefill_chunks_and_decode_steps_bit_exact():
     """uocr_page_coords against the oracle's coordinate rule: several
-    streams over several 256-token tiles with ragged tails, chunked calls
+    streams over several 1024-token tiles with ragged tails, chunked calls
     carrying the state, and one-token decode steps of a batch."""
     g = np.random.default_rng(0xC0)
     marker = 151
-    B, n = 5, 1000
+    B, n = 5, 2600
     dens = [0.0, 0.002, 0.05, 0.5, 1.0]
     toks = np.stack([np.where(g.random(n) < d, marker, g.integers(0, 150, n)) for d in dens]).astype(np.int32)
     start = np.stack([g.integers(0, 20, B), g.integers(-1, 500, B)], axis=1).astype(np.int32)
@@ -150,11 +150,11 @@ def test_page_coords_prefill_chunks_and_decode_steps_bit_exact():
         np.testing.assert_array_equal(tp[b], ot)
         np.testing.assert_array_equal(pp[b], op)
         assert tuple(st[b]) == os_
-    # one stream in chunks of 1, 255, 256, 257 and the rest, state carried on the device
+    # one stream in chunks of 1, 255, 1024, 1025 and the rest, state carried on the device
     s = start[3:4].copy()
     out_t, out_p = [], []
     a = 0
-    for c in [1, 255, 256, 257, n - 769]:
+    for c in [1, 255, 1024, 1025, n - 2305]:
         t_, p_, s = run(toks[3:4, a:a + c], s)
         out_t.append(t_[0])
         out_p.append(p_[0])
