@@ -6,13 +6,14 @@
 //
 // Rows of one chunk keep mostly different remote blocks, so a row-major
 // gather moves ~12 remote tiles per (row, head) through L2 with little reuse.
-// Here the (row, slot) pairs are bucketed by block (one workgroup, counting
-// sort in LDS), cut into chunks of at most 32 rows; one wave per (chunk,
-// head) reads the head's K and V tiles once, scores all rows of the chunk
-// with one chain of v_mfma_f32_32x32x16_bf16 (keys on M, rows on N, fp32
-// accumulation of exact bf16 products), takes the block's softmax per row
-// (max, exp2, sum: each lane owns 16 distinct scores of one row) and forms
-// P.V in fp32 (each lane two output dims over all 32 keys), writing the
+// Here the (row, slot) pairs are bucketed by block (a counting sort in LDS,
+// split over a few workgroups by block range), cut into chunks of at most
+// 32 rows; one wave per (chunk, head) reads the head's K and V tiles once,
+// scores all rows of the chunk with one chain of v_mfma_f32_32x32x16_bf16
+// (keys on M, rows on N, fp32 accumulation of exact bf16 products), takes
+// the block's softmax per row (max, exp2, sum: each lane owns 16 distinct
+// scores of one row) and forms P.V in fp32 (each lane two output dims over
+// all 32 keys), writing the
 // row's partial state (m, l, o[128]) for the slot.  The local window is
 // taken apart: a row's slots holding the window blocks of its own position
 // (shared by every row of a 32-row block) are attended per row block and
@@ -44,8 +45,6 @@ constexpr int kPartStride = kDim;               // o[128]: 512 B (four whole cac
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsView {
-  int32_t* off;    // [M+1] first pair of each block's bucket
-  int32_t* choff;  // [M+1] first chunk of each block; choff[M] = number of chunks
   int32_t* pairs;  // [T*topk] flat pair indices t*topk + s, bucketed by block
   int4* desc;      // [max_chunks] chunk descriptors: block j (-1: no chunk), first pair, rows, pool block
   float* part;     // [T][H][topk][kPartStride] unnormalised outputs o
@@ -54,8 +53,7 @@ struct WsView {
 
 __device__ __forceinline__ WsView ws_view(const PrefillAttnArgs& a) {
   unsigned char* w = static_cast<unsigned char*>(a.ws);
-  return {reinterpret_cast<int32_t*>(w + a.plan.off_off), reinterpret_cast<int32_t*>(w + a.plan.choff_off),
-          reinterpret_cast<int32_t*>(w + a.plan.pairs_off), reinterpret_cast<int4*>(w + a.plan.chunk_off),
+  return {reinterpret_cast<int32_t*>(w + a.plan.pairs_off), reinterpret_cast<int4*>(w + a.plan.chunk_off),
           reinterpret_cast<float*>(w + a.plan.part_off), reinterpret_cast<float2*>(w + a.plan.ml_off)};
 }
 
@@ -96,6 +94,21 @@ __device__ __forceinline__ int row_blocks(const AttnArgs& A) {
   return A.nq > 0 ? ((A.q_start + A.nq - 1) >> 5) - (A.q_start >> 5) + 1 : 0;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: inside each 16-lane
+// DPP row by shifts of 1, 2, 4 and 8 lanes (a lane shifted in from outside
+// the row adds 0), then the totals of the rows before (lanes 15, 31, 47).
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int lane = lane_id();
+  return x + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+
 // i / d for 0 <= i < 2^31 and 1 <= d: the high product with floor((2^32-1)/d)
 // is floor(i/d) or one less; one correction step fixes it.
 __device__ __forceinline__ int div_by(int i, int d, uint32_t magic) {
@@ -105,65 +118,125 @@ __device__ __forceinline__ int div_by(int i, int d, uint32_t magic) {
 }
 }  // namespace
 
-// Bucket the chunk's (row, slot) pairs by block: counts in LDS, one exclusive
-// scan for the bucket offsets and one for the chunk offsets (each thread owns
-// a contiguous range of blocks), then a scatter through LDS cursors.  The
-// order of pairs inside a bucket is not fixed, and does not need to be: each
-// pair's partial has its own slot.
+// Bucket the chunk's (row, slot) pairs by block.  Each of G workgroups
+// counts every pair into LDS (the atomics return each pair's rank in its
+// bucket) and scans the bucket sizes and their chunk counts (each thread
+// owns a contiguous range of blocks), so every workgroup knows where each
+// bucket starts without hearing from the others; workgroup g then writes
+// the chunk descriptors and the pairs of the blocks that wave g's threads
+// own, and nothing else.  The order of pairs inside a bucket is not fixed,
+// and does not need to be: each pair's partial has its own slot.
 //
-// Each thread loads its first kPairUnroll pairs in one round and keeps their
-// blocks (-1 where the slot does not count) in registers for the scatter, so
-// a chunk of up to kBucketThreads * kPairUnroll pairs (2048 rows x 16 slots)
-// reads block_idx once, with one memory round trip; larger chunks load the
-// rest in narrower rounds, once for the counts and again for the scatter.
-template <int N>
-__device__ __forceinline__ void bucket_round(const AttnArgs& A, int i0, int npairs, int topk, uint32_t magic, int M,
-                                             int lw, int (&jv)[N]) {
+// Each thread loads pairs 4 (tid + kBucketThreads u) .. +4 for
+// u < kPairUnroll / 4 (16-byte loads when block_idx is 16-byte aligned:
+// eight wide loads instead of 32 narrow ones per thread, the difference
+// between address-rate and latency bound for one workgroup) and keeps their
+// blocks (-1 where the slot does not count) in registers, so a chunk of up to
+// kBucketThreads * kPairUnroll pairs (2048 rows x 16 slots) reads block_idx
+// once per workgroup; larger chunks load the rest in narrower rounds, once
+// for the counts and again for the scatter.
+
+// Flat index of the pair a thread keeps in entry x of its first round: runs
+// of four pairs for 16-byte loads (VEC), else consecutive lanes take
+// consecutive pairs.
+template <bool VEC>
+__device__ __forceinline__ int first_round_pair(int tid, int x) {
+  return VEC ? 4 * (tid + (x >> 2) * kBucketThreads) + (x & 3) : tid + x * kBucketThreads;
+}
+
+// Block of pair i if its slot is bucketed (counts and is no window slot),
+// else -1.
+__device__ __forceinline__ int bucketed_block(const AttnArgs& A, int j, int i, uint32_t magic, int lw) {
+  const int p = A.q_start + div_by(i, A.topk, magic);
+  return j >= 0 && slot_counts(j, p, A.max_blocks) && !in_window(j, p, lw) ? j : -1;
+}
+
+// The first round's loads are branch-free (indices clamped into the array,
+// results past it replaced by -1) so that all of them are in flight at once.
+// VEC (chosen by the host): block_idx is 16-byte aligned and topk is a
+// multiple of 4, so each 16-byte load holds four slots of one row, whose
+// bucketing test is then 0 <= j <= min(max_blocks - 1, bp - lw) with bp the
+// block of the row's position (a slot counts iff j <= bp and is a window
+// slot iff bp - lw < j <= bp).
+template <bool VEC>
+__device__ __forceinline__ void first_round(const AttnArgs& A, int tid, int npairs, uint32_t magic, int lw,
+                                            int (&jv)[kPairUnroll]) {
+  if constexpr (VEC) {
 #pragma unroll
-  for (int u = 0; u < N; ++u) {
+    for (int u = 0; u < kPairUnroll / 4; ++u) {
+      const int i0 = first_round_pair<VEC>(tid, 4 * u);
+      const int4 v = *reinterpret_cast<const int4*>(A.block_idx + min(i0, npairs - 4));
+      const int bp = (A.q_start + div_by(i0, A.topk, magic)) >> 5;
+      const int top = i0 < npairs ? max(-1, min(A.max_blocks - 1, bp - max(lw, 0))) : -1;
+      const uint32_t n = (uint32_t)(top + 1);  // bucketed iff (unsigned)j < n
+      jv[4 * u] = (uint32_t)v.x < n ? v.x : -1;
+      jv[4 * u + 1] = (uint32_t)v.y < n ? v.y : -1;
+      jv[4 * u + 2] = (uint32_t)v.z < n ? v.z : -1;
+      jv[4 * u + 3] = (uint32_t)v.w < n ? v.w : -1;
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < kPairUnroll; ++x) {
+      const int i = first_round_pair<VEC>(tid, x);
+      const int v = A.block_idx[min(i, npairs - 1)];
+      jv[x] = i < npairs ? v : -1;
+    }
+#pragma unroll
+    for (int x = 0; x < kPairUnroll; ++x)
+      jv[x] = bucketed_block(A, jv[x], first_round_pair<VEC>(tid, x), magic, lw);
+  }
+}
+
+// A later round (chunks of more than kBucketThreads * kPairUnroll pairs):
+// pairs i0 + kBucketThreads u.
+__device__ __forceinline__ void tail_round(const AttnArgs& A, int i0, int npairs, uint32_t magic, int lw,
+                                           int (&jv)[kPairTail]) {
+#pragma unroll
+  for (int u = 0; u < kPairTail; ++u) {
     const int i = i0 + u * kBucketThreads;
     jv[u] = i < npairs ? A.block_idx[i] : -1;
   }
 #pragma unroll
-  for (int u = 0; u < N; ++u) {
-    const int i = i0 + u * kBucketThreads;
-    const int p = A.q_start + div_by(i, topk, magic);
-    if (jv[u] >= 0 && (!slot_counts(jv[u], p, M) || in_window(jv[u], p, lw))) jv[u] = -1;
-  }
+  for (int u = 0; u < kPairTail; ++u) jv[u] = bucketed_block(A, jv[u], i0 + u * kBucketThreads, magic, lw);
 }
 
 // CNT bounds max_blocks.  With STAGE > 0 (npairs <= STAGE, so every pair is
-// in the first round) the counting atomics return each pair's rank in its
-// bucket, the pairs go to bucket start + rank in an LDS copy of the pairs
-// array without a second round of atomics, and that copy is written out with
-// coalesced stores: one workgroup scattering 4-byte stores over the whole
-// pairs array touches a separate cache line per lane.
-template <int CNT, int STAGE>
+// in the first round) the workgroup's pairs go to bucket start + rank in an
+// LDS copy of its part of the pairs array, written out with coalesced
+// stores (4-byte stores scattered over the array would touch a separate
+// cache line per lane); otherwise they are scattered through LDS cursors.
+template <int CNT, int STAGE, bool VEC>
 __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(PrefillAttnArgs a) {
   static_assert(STAGE <= kBucketThreads * kPairUnroll, "staged pairs must all be in the first round");
   __shared__ int32_t s_cnt[CNT];
   __shared__ int32_t s_wsum[2][kBucketThreads / kWave];  // per-wave sums of the two scans
   __shared__ int32_t s_stage[STAGE > 0 ? STAGE : 1];
+  __shared__ int32_t s_range[2];  // the pairs of this workgroup's blocks: [s_range[0], s_range[1])
   const AttnArgs& A = a.attn;
   const WsView w = ws_view(a);
-  const int M = A.max_blocks, topk = A.topk;
+  const int M = A.max_blocks;
   const int tid = threadIdx.x;
+  const int g = blockIdx.x;
+  const int lw = a.plan.local_win;
   constexpr int kRound = kBucketThreads * kPairUnroll;
 
-  // Consecutive lanes take consecutive pairs (slots of a few rows), which keeps
-  // same-block LDS atomics within a wave to a few lanes.
-  const int npairs = A.nq * topk;
-  const uint32_t magic = 0xFFFFFFFFu / (uint32_t)topk;
-  // the pool indices of this thread's blocks (for the descriptors), read
-  // now so that the load overlaps the pair loads and the counting
+  const int npairs = A.nq * A.topk;
+  const uint32_t magic = 0xFFFFFFFFu / (uint32_t)A.topk;
   constexpr int kSeg = (CNT + kBucketThreads - 1) / kBucketThreads;
   const int seg = (M + kBucketThreads - 1) / kBucketThreads;  // <= kSeg
   const int j0 = min(tid * seg, M), j1 = min(j0 + seg, M);
-  int pbs[kSeg];
+  const bool own = tid / kWave == g;  // this thread's blocks are this workgroup's
+  const int jlo = min(g * kWave * seg, M), jhi = min((g + 1) * kWave * seg, M);
+  // pool indices of this thread's own blocks (for the descriptors; sequence
+  // 0), read now so that the load overlaps the pair loads and the counting
+  // (for up to 4 blocks per thread; more would crowd out the pairs)
+  constexpr int kPre = kSeg <= 4 ? kSeg : 1;
+  int pbs[kPre];
 #pragma unroll
-  for (int k = 0; k < kSeg; ++k) pbs[k] = j0 + k < j1 ? A.block_table[j0 + k] : -1;  // sequence 0
+  for (int k = 0; k < kPre; ++k) pbs[k] = kSeg <= 4 ? A.block_table[min(j0 + k, M - 1)] : -1;
   int jf[kPairUnroll];  // the first round's blocks, kept for the scatter
-  bucket_round(A, tid, npairs, topk, magic, M, a.plan.local_win, jf);
+  constexpr bool kVec = VEC && STAGE > 0;  // wide loads where the registers allow
+  first_round<kVec>(A, tid, npairs, magic, lw, jf);
   for (int j = tid; j < M; j += kBucketThreads) s_cnt[j] = 0;
   __syncthreads();
   int rk[kPairUnroll];  // STAGE > 0: each pair's rank in its bucket
@@ -178,7 +251,7 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
   if constexpr (STAGE == 0) {
     for (int i0 = tid + kRound; i0 < npairs; i0 += kBucketThreads * kPairTail) {
       int jv[kPairTail];
-      bucket_round(A, i0, npairs, topk, magic, M, a.plan.local_win, jv);
+      tail_round(A, i0, npairs, magic, lw, jv);
 #pragma unroll
       for (int u = 0; u < kPairTail; ++u)
         if (jv[u] >= 0) atomicAdd(&s_cnt[jv[u]], 1);
@@ -192,77 +265,70 @@ __global__ __launch_bounds__(kBucketThreads) void attn_prefill_bucket_kernel(Pre
     sp += c;
     sc += (c + kRowsPerChunk - 1) / kRowsPerChunk;
   }
-  // exclusive scans of both sums: within each wave by lane shifts, then over
-  // the 16 wave sums (one barrier instead of two per doubling step)
-  const int lane = tid & (kWave - 1), wv = tid / kWave;
-  int ip = sp, ic = sc;
-#pragma unroll 1
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int xp = __shfl_up(ip, d, kWave), xc = __shfl_up(ic, d, kWave);
-    if (lane >= d) {
-      ip += xp;
-      ic += xc;
-    }
-  }
+  // exclusive scans of both sums: within each wave, then over the 16 wave
+  // sums (held by lanes 0-15 of every wave after one barrier)
+  constexpr int kWaves = kBucketThreads / kWave;
+  const int lane = tid & (kWave - 1), wv = wave_id();
+  const int ip = wave_incl_sum(sp), ic = wave_incl_sum(sc);
   if (lane == kWave - 1) {
     s_wsum[0][wv] = ip;
     s_wsum[1][wv] = ic;
   }
   __syncthreads();
-  int tot_p = 0, tot_c = 0, before_p = 0, before_c = 0;
-#pragma unroll 1
-  for (int w_ = 0; w_ < kBucketThreads / kWave; ++w_) {  // not unrolled: the pairs held in registers leave no room
-    const int x0 = s_wsum[0][w_], x1 = s_wsum[1][w_];
-    before_p += w_ < wv ? x0 : 0;
-    before_c += w_ < wv ? x1 : 0;
-    tot_p += x0;
-    tot_c += x1;
-  }
+  const int wp = wave_incl_sum(lane < kWaves ? s_wsum[0][lane] : 0);
+  const int wc = wave_incl_sum(lane < kWaves ? s_wsum[1][lane] : 0);
+  const int before_p = wv > 0 ? __builtin_amdgcn_readlane(wp, wv - 1) : 0;
+  const int before_c = wv > 0 ? __builtin_amdgcn_readlane(wc, wv - 1) : 0;
+  const int tot_c = __builtin_amdgcn_readlane(wc, kWaves - 1);
   int po = before_p + ip - sp, co = before_c + ic - sc;
-#pragma unroll
-  for (int k = 0; k < kSeg; ++k) {
+  if (own && lane == 0) s_range[0] = po;
+  if (own && lane == kWave - 1) s_range[1] = po + sp;
+  // the descriptors of the thread's own blocks; s_cnt becomes each bucket's
+  // cursor
+  auto block_descs = [&](int k, int pb_pre) {
     const int j = j0 + k;
-    if (j >= j1) break;
     const int c = s_cnt[j];
     const int nch = (c + kRowsPerChunk - 1) / kRowsPerChunk;
-    w.off[j] = po;
-    w.choff[j] = co;
-    if (nch > 0) {
-      const int pb = pbs[k];
+    if (own && nch > 0) {
+      const int pb = kSeg <= 4 ? pb_pre : A.block_table[j];
       for (int q = 0; q < nch; ++q)
         w.desc[co + q] = make_int4(j, po + q * kRowsPerChunk, min(kRowsPerChunk, c - q * kRowsPerChunk), pb);
     }
-    s_cnt[j] = po;  // becomes the bucket's cursor
+    s_cnt[j] = po;
     po += c;
     co += nch;
+  };
+  if constexpr (kSeg <= 4) {
+#pragma unroll
+    for (int k = 0; k < kSeg; ++k)
+      if (j0 + k < j1) block_descs(k, pbs[k]);
+  } else {
+#pragma unroll 1
+    for (int k = 0; j0 + k < j1; ++k) block_descs(k, -1);
   }
-  if (tid == kBucketThreads - 1) {
-    w.off[M] = tot_p;
-    w.choff[M] = tot_c;
-  }
-  // descriptors past the last chunk: none
-  for (int g = tot_c + tid; g < a.plan.max_chunks; g += kBucketThreads)
-    w.desc[g] = make_int4(-1, 0, 0, -1);
+  // descriptors past the last chunk: none (spread over the workgroups)
+  for (int x = tot_c + g * kBucketThreads + tid; x < a.plan.max_chunks; x += (int)gridDim.x * kBucketThreads)
+    w.desc[x] = make_int4(-1, 0, 0, -1);
   __syncthreads();
   if constexpr (STAGE > 0) {
-    // s_cnt now holds each bucket's first position; start + rank stays below
-    // the number of counted pairs (<= npairs <= STAGE).
+    // s_cnt holds each bucket's first position; start + rank - lo stays
+    // below hi - lo <= npairs <= STAGE.
+    const int lo = s_range[0], hi = s_range[1];
 #pragma unroll
     for (int u = 0; u < kPairUnroll; ++u)
-      if (jf[u] >= 0) s_stage[s_cnt[jf[u]] + rk[u]] = tid + u * kBucketThreads;
+      if (jf[u] >= jlo && jf[u] < jhi) s_stage[s_cnt[jf[u]] + rk[u] - lo] = first_round_pair<kVec>(tid, u);
     __syncthreads();
-    const int total = tot_p;
-    for (int k = tid; k < total; k += kBucketThreads) w.pairs[k] = s_stage[k];
+    for (int k = tid; k < hi - lo; k += kBucketThreads) w.pairs[lo + k] = s_stage[k];
   } else {
 #pragma unroll
     for (int u = 0; u < kPairUnroll; ++u)
-      if (jf[u] >= 0) w.pairs[atomicAdd(&s_cnt[jf[u]], 1)] = tid + u * kBucketThreads;
+      if (jf[u] >= jlo && jf[u] < jhi) w.pairs[atomicAdd(&s_cnt[jf[u]], 1)] = first_round_pair<kVec>(tid, u);
     for (int i0 = tid + kRound; i0 < npairs; i0 += kBucketThreads * kPairTail) {
       int jv[kPairTail];
-      bucket_round(A, i0, npairs, topk, magic, M, a.plan.local_win, jv);
+      tail_round(A, i0, npairs, magic, lw, jv);
 #pragma unroll
       for (int u = 0; u < kPairTail; ++u)
-        if (jv[u] >= 0) w.pairs[atomicAdd(&s_cnt[jv[u]], 1)] = i0 + u * kBucketThreads;
+        if (jv[u] >= jlo && jv[u] < jhi) w.pairs[atomicAdd(&s_cnt[jv[u]], 1)] = i0 + u * kBucketThreads;
     }
   }
 }
@@ -727,10 +793,6 @@ PrefillAttnPlan prefill_attn_plan(int32_t T, int32_t heads, int32_t topk, int32_
   if (npairs >= ((int64_t)1 << 31) / 2) return p;  // flat pair indices stay in int32
   p.max_chunks = (int32_t)(max_blocks + (npairs + kRowsPerChunk - 1) / kRowsPerChunk);
   size_t at = 0;
-  p.off_off = at;
-  at = align256(at + (size_t)(max_blocks + 1) * 4);
-  p.choff_off = at;
-  at = align256(at + (size_t)(max_blocks + 1) * 4);
   p.pairs_off = at;
   at = align256(at + (size_t)npairs * 4);
   p.chunk_off = at;
@@ -749,7 +811,7 @@ int row_blocks_host(const AttnArgs& A) {
 }
 
 // The window pass does not depend on the bucketing, and the bucketing runs
-// in one workgroup, so the window pass runs beside it on a second stream
+// in a few workgroups, so the window pass runs beside it on a second stream
 // (default priority, non-blocking), forked from and joined back to the
 // caller's stream with two events: one stream and two events per device,
 // created on first use and held until the process ends.  A mutex per device
@@ -797,12 +859,19 @@ hipError_t launch_attn_prefill_blocks(const PrefillAttnArgs& a, hipStream_t stre
   } else if (lunits > 0) {
     hipLaunchKernelGGL(attn_prefill_local_kernel, lgrid, dim3(kBlockWaves * kWave), 0, stream, a);
   }
-  // Staged bucketing: counts for up to 4096 blocks (16 KB) and up to 32768
-  // pairs (128 KB) in LDS, beside the 8 KB scan.
-  if (A.max_blocks <= 4096 && (int64_t)A.nq * A.topk <= 32768)
-    hipLaunchKernelGGL((attn_prefill_bucket_kernel<4096, 32768>), dim3(1), dim3(kBucketThreads), 0, stream, a);
+  // One bucketing workgroup per wave's worth of blocks in the scan (at most
+  // 16).  Staged bucketing: counts for up to 4096 blocks (16 KB) and up to
+  // 32768 pairs (128 KB) in LDS, beside the 8 KB scan.
+  const int seg = (A.max_blocks + kBucketThreads - 1) / kBucketThreads;
+  const dim3 bgrid((unsigned)((A.max_blocks + kWave * seg - 1) / (kWave * seg)));
+  const int64_t npairs = (int64_t)A.nq * A.topk;
+  const bool vec = (reinterpret_cast<uintptr_t>(A.block_idx) & 15) == 0 && A.topk % 4 == 0;
+  if (A.max_blocks <= 4096 && npairs <= 32768 && vec)
+    hipLaunchKernelGGL((attn_prefill_bucket_kernel<4096, 32768, true>), bgrid, dim3(kBucketThreads), 0, stream, a);
+  else if (A.max_blocks <= 4096 && npairs <= 32768)
+    hipLaunchKernelGGL((attn_prefill_bucket_kernel<4096, 32768, false>), bgrid, dim3(kBucketThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_prefill_bucket_kernel<kMaxBlocksAttnBucket, 0>), dim3(1), dim3(kBucketThreads), 0,
+    hipLaunchKernelGGL((attn_prefill_bucket_kernel<kMaxBlocksAttnBucket, 0, false>), bgrid, dim3(kBucketThreads), 0,
                        stream, a);
   const int64_t units = (int64_t)a.plan.max_chunks * A.heads;
   hipLaunchKernelGGL(attn_prefill_block_kernel, dim3((unsigned)((units + kBlockWaves - 1) / kBlockWaves)),

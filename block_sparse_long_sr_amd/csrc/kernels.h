@@ -63,7 +63,7 @@ constexpr int32_t kMaxBlocksAttnBucket = 16384;  // bucket counts live in LDS
 struct PrefillAttnPlan {
   int32_t max_chunks;  // upper bound of the number of row chunks
   int32_t local_win;   // window blocks attended per row block (the local window; 0: none), set by the caller
-  size_t off_off, choff_off, pairs_off, chunk_off, part_off, ml_off;  // byte offsets in the workspace
+  size_t pairs_off, chunk_off, part_off, ml_off;  // byte offsets in the workspace
   size_t ws_bytes;     // 0: sizes not supported by this path
 };
 PrefillAttnPlan prefill_attn_plan(int32_t T, int32_t heads, int32_t topk, int32_t max_blocks);
