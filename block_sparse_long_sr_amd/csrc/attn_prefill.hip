@@ -94,21 +94,6 @@ __device__ __forceinline__ int row_blocks(const AttnArgs& A) {
   return A.nq > 0 ? ((A.q_start + A.nq - 1) >> 5) - (A.q_start >> 5) + 1 : 0;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave: inside each 16-lane
-// DPP row by shifts of 1, 2, 4 and 8 lanes (a lane shifted in from outside
-// the row adds 0), then the totals of the rows before (lanes 15, 31, 47).
-__device__ __forceinline__ int wave_incl_sum(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
-  const int r0 = __builtin_amdgcn_readlane(x, 15);
-  const int r1 = __builtin_amdgcn_readlane(x, 31);
-  const int r2 = __builtin_amdgcn_readlane(x, 47);
-  const int lane = lane_id();
-  return x + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
-}
-
 // i / d for 0 <= i < 2^31 and 1 <= d: the high product with floor((2^32-1)/d)
 // is floor(i/d) or one less; one correction step fixes it.
 __device__ __forceinline__ int div_by(int i, int d, uint32_t magic) {

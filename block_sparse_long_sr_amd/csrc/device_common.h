@@ -108,6 +108,22 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Inclusive prefix sum over the 64 lanes of a wave: inside each 16-lane
+// DPP row by shifts of 1, 2, 4 and 8 lanes (a lane shifted in from outside
+// the row adds 0), then the totals of the rows before (lanes 15, 31, 47).
+// Every lane of the wave takes part.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int lane = lane_id();
+  return x + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+
 __device__ __forceinline__ int clamp_ctx(int32_t L, int32_t max_blocks) {
   const int hi = max_blocks * kBlock;
   return L < 0 ? 0 : (L > hi ? hi : L);
