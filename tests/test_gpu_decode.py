@@ -37,6 +37,23 @@ def test_edge_lengths_ragged_batch():
     G.full_decode_check(dev, wl, 0, 0, range(wl.batch), G.cfg_for(wl), G.ocfg())
 
 
+def test_batches_at_and_above_256_sequences():
+    """The decode indexer numbers only the live (sequence, chunk) units for
+    batches of up to 256 sequences and takes every unit above that: a
+    256-sequence and a 300-sequence batch of short, ragged contexts (empty
+    ones and ones inside the local window included), checked on a sample of
+    sequences (every score, -inf entries included; selection; attention)."""
+    g = np.random.default_rng(0xE9)
+    for B in (256, 300):
+        lens = g.integers(0, 3000, B)
+        lens[:6] = [0, 1, 100, 129, 2999, 0]
+        wl = _wl(f"decode batch {B}", 0xE9 + B, lens)
+        print("case:", wl.name, flush=True)
+        dev = SD.generate(wl)
+        seqs = sorted(set([0, 1, 2, 3, 4, 5, B - 1] + [int(x) for x in g.choice(B, 20, replace=False)]))
+        G.full_decode_check(dev, wl, 0, 0, seqs, G.cfg_for(wl), G.ocfg())
+
+
 def test_several_tiles_and_ragged_tail():
     wl = _wl("ragged 3 seqs", 0xE2, [32768, 20001, 9999], layers=2)
     print("case: decode ragged S<=32768, 2 layers", flush=True)

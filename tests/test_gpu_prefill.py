@@ -220,6 +220,38 @@ def test_prefill_attention_block_major_matches_row_major_and_oracle():
         G.check_attention(res_b["out"][t], res_b["lse"][t], o2, l2)
 
 
+def test_prefill_block_major_unaligned_block_idx():
+    """block_idx at a 4-byte offset (not 16-byte aligned) sends the bucketing
+    down its narrow-load path: the output equals the aligned call's bit for
+    bit (each pair's partial has its own slot, so the order of the pairs in
+    a bucket never reaches the result), and both match the oracle."""
+    wl = W.prefill_case("prefill unaligned block_idx S=4700 q_start=3000 T=1700", 0xFA, 4700, 3000, 1700)
+    print("case:", wl.name, flush=True)
+    cfg_u, cfg_o = G.cfg_for(wl), G.ocfg()
+    topk = cfg_u.topk_blocks
+    dev = SD.generate(wl)
+    res = G.gpu_prefill(dev, cfg_u)
+    T, M, H, D = wl.rows, wl.max_blocks, wl.heads, wl.head_dim
+    buf = torch.full((T * topk + 1,), -7, dtype=torch.int32, device="cuda")
+    idx_u = buf[1:].view(T, topk)
+    idx_u.copy_(torch.from_numpy(res["idx"]).cuda())
+    assert idx_u.data_ptr() % 16 != 0
+    ab = U.workspace_size(cfg_u, U.OP_ATTN_PREFILL, T, M)
+    aws = torch.full((ab,), 0x3C, dtype=torch.uint8, device="cuda")
+    out = torch.full((T, H, D), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    U.sparse_attn_prefill(cfg_u, dev.kv(0), dev.q, wl.q_start, T, idx_u, out, lse, ws=aws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), res["out"])
+    np.testing.assert_array_equal(lse.cpu().numpy(), res["lse"])
+    allrows = np.arange(T)
+    q = wl.q_rows(allrows)
+    for t in range(0, T, 211):
+        got = [int(x) for x in res["idx"][t] if x >= 0]
+        o2, l2 = G.oracle_attend_with(wl, 0, 0, q[t], got, wl.q_start + t, cfg_o)
+        G.check_attention(res["out"][t], res["lse"][t], o2, l2)
+
+
 def test_prefill_attention_graph_capture_and_concurrent_streams():
     """The block-major prefill attention forks its window pass onto a second
     stream and joins it back: captured in a HIP graph and replayed with eager
