@@ -406,41 +406,40 @@ hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t strea
 // l ^ 32), not LDS permutes, so a round is a short chain of VALU ops.
 // ---------------------------------------------------------------------------
 
+// A 64-bit key of the lane's DPP partner (both halves moved with the same
+// control; every lane has a source for the patterns used below).
 template <int kCtrl>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false);
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, kCtrl, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), kCtrl, 0xF, 0xF, true);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// Larger of (hi, lo) and the pair another lane holds, compared as one 64-bit
-// value.
-__device__ __forceinline__ void take_larger(uint32_t& hi, uint32_t& lo, uint32_t ohi, uint32_t olo) {
-  const bool take = ohi > hi || (ohi == hi && olo > lo);
-  hi = take ? ohi : hi;
-  lo = take ? olo : lo;
+__device__ __forceinline__ uint64_t larger_u64(uint64_t a, uint64_t b) { return b > a ? b : a; }
+
+// Larger of the lane's key and the one of lane l ^ 16 (l ^ 32 with W = 32):
+// v_permlane*_swap of (x, x) leaves both values in every lane.
+template <int W>
+__device__ __forceinline__ uint64_t swap_larger(uint64_t k) {
+  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+  const auto l2 = W == 16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                          : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto h2 = W == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                          : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  return larger_u64(((uint64_t)h2[0] << 32) | l2[0], ((uint64_t)h2[1] << 32) | l2[1]);
 }
 
-// Every lane gets the wave's largest (hi, lo).
-__device__ __forceinline__ void wave_max_pair(uint32_t& hi, uint32_t& lo) {
-  take_larger(hi, lo, dpp_u32<0xB1>(hi), dpp_u32<0xB1>(lo));    // quad_perm [1,0,3,2]
-  take_larger(hi, lo, dpp_u32<0x4E>(hi), dpp_u32<0x4E>(lo));    // quad_perm [2,3,0,1]
-  take_larger(hi, lo, dpp_u32<0x141>(hi), dpp_u32<0x141>(lo));  // row_half_mirror
-  take_larger(hi, lo, dpp_u32<0x140>(hi), dpp_u32<0x140>(lo));  // row_mirror
-  {
-    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-    uint32_t h0 = h[0], l0 = l[0];
-    take_larger(h0, l0, h[1], l[1]);
-    hi = h0;
-    lo = l0;
-  }
-  {
-    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-    uint32_t h0 = h[0], l0 = l[0];
-    take_larger(h0, l0, h[1], l[1]);
-    hi = h0;
-    lo = l0;
-  }
+// Every lane gets the wave's largest key: a quad (two quad permutations),
+// the halves of a row, the two halves of each 16-lane row, then lanes l ^ 16
+// and l ^ 32; each step is two lane moves, one 64-bit compare and two
+// selects.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  k = larger_u64(k, dpp_u64<0xB1>(k));   // quad_perm [1,0,3,2]
+  k = larger_u64(k, dpp_u64<0x4E>(k));   // quad_perm [2,3,0,1]
+  k = larger_u64(k, dpp_u64<0x141>(k));  // row_half_mirror
+  k = larger_u64(k, dpp_u64<0x140>(k));  // row_mirror
+  k = swap_larger<16>(k);
+  return swap_larger<32>(k);
 }
 
 template <int R>
@@ -483,33 +482,25 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(TopkPrefillArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) kp[r] = 0u;
   }
-  uint32_t lk[R];
-  int32_t li[R];
+  // Composite rank keys (truncated score, 0xFFFFFFFF - block id), unique and
+  // descending in each lane; empty slots 0.
+  uint64_t ck[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    lk[r] = kp[r] >> P.idbits;  // >= 1 for every real candidate
-    li[r] = kp[r] != 0u ? lane * P.bps + (int32_t)(idmask - (kp[r] & idmask)) : -1;
+    const uint32_t id = (uint32_t)(lane * P.bps) + (idmask - (kp[r] & idmask));
+    ck[r] = kp[r] != 0u ? ((uint64_t)(kp[r] >> P.idbits) << 32) | (0xFFFFFFFFu - id) : 0ull;
   }
 
   int32_t mine = -1;  // lane w keeps the w-th winner
 #pragma unroll
   for (int w = 0; w < R; ++w) {
-    // Composite rank key: (truncated score, 0xFFFFFFFF - id); empty = (0, 0).
-    uint32_t hi = li[0] >= 0 ? lk[0] : 0u;
-    uint32_t lo = li[0] >= 0 ? 0xFFFFFFFFu - (uint32_t)li[0] : 0u;
-    const uint32_t my_hi = hi, my_lo = lo;
-    wave_max_pair(hi, lo);
-    if (hi == 0u && lo == 0u) break;
-    const int32_t id = (int32_t)(0xFFFFFFFFu - lo);
-    if (lane == w) mine = id;
-    if (my_hi == hi && my_lo == lo) {
+    const uint64_t best = wave_max_u64(ck[0]);
+    if (best == 0ull) break;
+    if (lane == w) mine = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
+    if (ck[0] == best) {  // the one lane that held it moves to its next entry
 #pragma unroll
-      for (int r = 0; r + 1 < R; ++r) {
-        lk[r] = lk[r + 1];
-        li[r] = li[r + 1];
-      }
-      lk[R - 1] = 0u;
-      li[R - 1] = -1;
+      for (int r = 0; r + 1 < R; ++r) ck[r] = ck[r + 1];
+      ck[R - 1] = 0ull;
     }
   }
 
