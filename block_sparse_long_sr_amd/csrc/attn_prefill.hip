@@ -112,14 +112,14 @@ __device__ __forceinline__ int div_by(int i, int d, uint32_t magic) {
 // own, and nothing else.  The order of pairs inside a bucket is not fixed,
 // and does not need to be: each pair's partial has its own slot.
 //
-// Each thread loads pairs 4 (tid + kBucketThreads u) .. +4 for
-// u < kPairUnroll / 4 (16-byte loads when block_idx is 16-byte aligned:
-// eight wide loads instead of 32 narrow ones per thread, the difference
-// between address-rate and latency bound for one workgroup) and keeps their
-// blocks (-1 where the slot does not count) in registers, so a chunk of up to
+// Each thread keeps kPairUnroll pairs of the first round in registers
+// (their blocks, -1 where the slot is not bucketed), so a chunk of up to
 // kBucketThreads * kPairUnroll pairs (2048 rows x 16 slots) reads block_idx
 // once per workgroup; larger chunks load the rest in narrower rounds, once
-// for the counts and again for the scatter.
+// for the counts and again for the scatter.  With 16-byte loads of four
+// slots of one row (first_round), the row's bucketing bound is computed once
+// per four slots: on one compute unit the per-slot division and tests, not
+// the loads, were the first round's cost.
 
 // Flat index of the pair a thread keeps in entry x of its first round: runs
 // of four pairs for 16-byte loads (VEC), else consecutive lanes take
