@@ -14,11 +14,7 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* scratc
   constexpr int kWaves = NT / kWave;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    uint32_t o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
+  v = (uint32_t)wave_incl_sum((int)v);
   if (lane == kWave - 1) scratch[wave] = v;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -92,12 +88,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t remain
       c[i] = hist[255 - 4 * lane - i];
       sum += c[i];
     }
-    uint32_t incl = sum;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const uint32_t o = __shfl_up(incl, d, kWave);
-      if (lane >= d) incl += o;
-    }
+    const uint32_t incl = (uint32_t)wave_incl_sum((int)sum);
     uint32_t cum = incl - sum;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
