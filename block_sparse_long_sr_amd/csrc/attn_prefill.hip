@@ -424,9 +424,7 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_block_kernel
       *reinterpret_cast<float4*>(P + n * kPStride + 8 * q4 + 4 * hh) =
           make_float4(z[4 * q4], z[4 * q4 + 1], z[4 * q4 + 2], z[4 * q4 + 3]);
     // Largest position among the chunk's rows: keys past it are masked for all.
-    int pmax = n < n_rows ? p_n : -1;
-#pragma unroll
-    for (int m_ = 1; m_ < kWave; m_ <<= 1) pmax = max(pmax, __shfl_xor(pmax, m_, kWave));
+    const int pmax = wave_max_i32(n < n_rows ? p_n : -1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const bool seen = j * kBlock + 4 * i + kg <= pmax;
@@ -724,9 +722,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void attn_prefill_merge_kernel
     const bool valid = s < A.topk && slot_counts(js, p, A.max_blocks) && (!in_window(js, p, lw) || s == sfirst);
     float2 ml = make_float2(-INFINITY, 0.0f);
     if (valid) ml = mls[s];
-    float Mr = ml.x;
-#pragma unroll
-    for (int m_ = 1; m_ < kWave; m_ <<= 1) Mr = fmaxf(Mr, __shfl_xor(Mr, m_, kWave));
+    const float Mr = wave_max_f32(ml.x);
     if (Mr == -INFINITY) continue;
     // rescale what earlier rounds accumulated
     const float Mn = fmaxf(M, Mr);
@@ -736,10 +732,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void attn_prefill_merge_kernel
     L *= sc;
     M = Mn;
     const float f = valid ? exp2f(ml.x - M) : 0.0f;
-    float lf = ml.y * f;
-#pragma unroll
-    for (int m_ = 1; m_ < kWave; m_ <<= 1) lf += __shfl_xor(lf, m_, kWave);
-    L += lf;
+    L += wave_sum_f32(ml.y * f);
     const int ns = min(kWave, A.topk - s0);
     for (int u0 = 0; u0 < ns; u0 += 16) {
       float o0[16], o1[16], fu[16];

@@ -62,6 +62,20 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 __device__ __forceinline__ float shfl_xor_f32(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// Maximum over the 16 lanes of a DPP row (the exchanges of row16_sum).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  return fmaxf(v, dpp_f32<0x140>(v));
+}
+__device__ __forceinline__ int row16_max_i32(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));
+  return max(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));
+}
+
 // Combine a value with the one of lane l ^ 16 (or l ^ 32), in every lane,
 // with the gfx950 lane swaps (one VALU op each, no LDS permute).  With both
 // operands x, element 0 + element 1 of v_permlane16_swap is x[l] + x[l ^ 16]
@@ -88,6 +102,18 @@ __device__ __forceinline__ uint32_t sum_xor16_u32(uint32_t x) {
 __device__ __forceinline__ uint32_t sum_xor32_u32(uint32_t x) {
   const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   return r[0] + r[1];
+}
+
+// Sum, maximum over all 64 lanes of a wave, in every lane: the DPP row
+// reduction, then the lane swaps across rows (no LDS permutes).
+__device__ __forceinline__ float wave_sum_f32(float v) { return sum_xor32(sum_xor16(row16_sum(v))); }
+__device__ __forceinline__ float wave_max_f32(float v) { return max_xor32(max_xor16(row16_max(v))); }
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = row16_max_i32(v);
+  auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = max((int)r[0], (int)r[1]);
+  r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return max((int)r[0], (int)r[1]);
 }
 
 // Block-max reduction of key scores: NaN-propagating maximum (a block with a
