@@ -389,6 +389,7 @@ int decode_step_common(const uocr_sparse_cfg* cfg, const uocr_kv* kv, int32_t n_
   a.local_blocks = cfg->local_blocks;
   a.lag = plan.lag;
   a.chunk = plan.chunk;
+  a.poll_sel = plan.poll_sel;
   a.scale_log2 = cfg->sm_scale * 1.44269504088896340736f;
   return hip_status(uocr::launch_decode_step(a, plan, one_launch, static_cast<hipStream_t>(stream)), name);
 }

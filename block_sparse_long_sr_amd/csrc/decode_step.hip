@@ -54,6 +54,7 @@ constexpr int kStepWaves = kStepThreads / kWave;
 constexpr int kMaxStepChunk = 32;  // blocks per scoring item, at most
 constexpr uint32_t kSpinLimit = 1u << 20;  // polls of one wait: a device-scope load (~1 us) + s_sleep 2 each, about a second
 constexpr int kTableCache = 4096;  // block-table rows up to this many entries are read into LDS
+constexpr int32_t kSelPending = INT32_MIN;  // an id slot not yet published (never a valid output)
 
 struct Item {
   int attention;  // 0: scoring item, 1: attention item
@@ -97,6 +98,31 @@ __device__ __forceinline__ void wait_count(uint32_t* ctr, uint32_t need, uint32_
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
+// Wave 0 only: poll the topk published ids of a slot (device-scope loads)
+// until none is kSelPending, and copy them to LDS.  Bounded like wait_count.
+__device__ __forceinline__ void wait_ids(const int32_t* sel, int topk, int32_t* s_out, uint32_t* err,
+                                         int32_t* status_out) {
+  const int lane = lane_id();
+  for (int i0 = 0; i0 < topk; i0 += kWave) {
+    const int i = i0 + lane;
+    int32_t v = 0;
+    bool done = false;
+    for (uint32_t it = 0; it < kSpinLimit; ++it) {
+      v = i < topk ? __hip_atomic_load(sel + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+      if (__ballot(v == kSelPending) == 0) {
+        done = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (!done && lane == 0) {
+      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (status_out != nullptr) __hip_atomic_store(status_out, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (i < topk) s_out[i] = v;
+  }
+}
+
 // Device-scope (write-through) store of a value other workgroups read.
 template <typename T>
 __device__ __forceinline__ void publish(T* p, T v) {
@@ -124,9 +150,13 @@ __device__ __forceinline__ uint32_t count_done(uint32_t* ctr) {
 }
 }  // namespace
 
+// Zeroes the counters and, for a launch whose attention items poll the
+// published ids, fills the id output with kSelPending.
 __global__ __launch_bounds__(kStepThreads) void decode_step_clear_kernel(uint32_t* counters, int n,
-                                                                         int32_t* status_out) {
+                                                                         int32_t* status_out, int32_t* sel,
+                                                                         int64_t nsel) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) counters[i] = 0u;
+  for (int64_t i = threadIdx.x; i < nsel; i += blockDim.x) sel[i] = kSelPending;
   if (status_out != nullptr && threadIdx.x == 0) *status_out = 0;
 }
 
@@ -238,9 +268,15 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
       const bool cached = M <= kTableCache;
       if (cached)
         for (int i = tid; i < M; i += kStepThreads) s_table[i] = table[i];
-      if (tid == 0) wait_count<true>(sel_done + it.slot, 1u, err, a.status_out);
-      __syncthreads();
-      for (int i = tid; i < a.topk; i += kStepThreads) s_blocks[i] = sel_out[i];
+      if (a.poll_sel) {
+        // the ids themselves are polled: one round trip fewer than the
+        // counter, a fence and a read of the ids
+        if (wave == 0) wait_ids(sel_out, a.topk, s_blocks, err, a.status_out);
+      } else {
+        if (tid == 0) wait_count<true>(sel_done + it.slot, 1u, err, a.status_out);
+        __syncthreads();
+        for (int i = tid; i < a.topk; i += kStepThreads) s_blocks[i] = sel_out[i];
+      }
       __syncthreads();
       const int h = it.idx;
       const int64_t head_row = (int64_t)it.slot * H + h;
@@ -280,6 +316,12 @@ DecodeStepPlan decode_step_plan(int32_t n_layers, int32_t batch, int32_t heads, 
   // latency every step of the chain sees (16 x 12 x 32K: 447-464 us against
   // 598 us with two; at 128K two are better, 1103 against 1138 us).
   p.groups_per_cu = max_blocks >= 2048 ? 2 : 1;
+  // Attention items poll the published ids directly (the id output is
+  // filled with kSelPending before the launch) where the layer chain sets
+  // the pace: one memory round trip less per layer (16 x 12 x 32K: 398-406
+  // against 408-414 us); at long contexts, where bandwidth does, it measured
+  // 0-20 us slower than the counter, which stays there.
+  p.poll_sel = p.groups_per_cu == 1 ? 1 : 0;
   p.counter_words = 2 + 3 * S;
   p.ws_bytes = (size_t)((p.counter_words * 4 + 255) / 256 * 256);
   p.items = S * (((int64_t)max_blocks + p.chunk - 1) / p.chunk + heads);
@@ -369,7 +411,7 @@ hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& pla
     // only needs its 0)
     if (a.status_out != nullptr) {
       hipLaunchKernelGGL(decode_step_clear_kernel, dim3(1), dim3(kStepThreads), 0, stream, a.counters, 0,
-                         a.status_out);
+                         a.status_out, a.block_idx, (int64_t)0);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -417,7 +459,8 @@ hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& pla
     return hipSuccess;
   }
   hipLaunchKernelGGL(decode_step_clear_kernel, dim3(1), dim3(kStepThreads), 0, stream, a.counters,
-                     (int)plan.counter_words, a.status_out);
+                     (int)plan.counter_words, a.status_out, a.block_idx,
+                     a.poll_sel ? (int64_t)a.n_layers * a.batch * a.topk : (int64_t)0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t max_cand = (int64_t)a.max_blocks - a.local_blocks;

@@ -122,6 +122,7 @@ struct DecodeStepArgs {
   int32_t local_blocks;
   int32_t lag;
   int32_t chunk;               // blocks per scoring item, a multiple of 16
+  int32_t poll_sel;            // 1: attention items poll block_idx itself (cleared to INT32_MIN first)
   float scale_log2;
 };
 struct DecodeStepPlan {
@@ -130,6 +131,7 @@ struct DecodeStepPlan {
   int64_t counter_words;  // 2 + 3 * n_layers * batch
   int64_t items;          // work items of the launch
   int32_t groups_per_cu;  // resident workgroups per compute unit
+  int32_t poll_sel;       // attention items poll the published ids (see DecodeStepArgs)
   size_t ws_bytes;
 };
 DecodeStepPlan decode_step_plan(int32_t n_layers, int32_t batch, int32_t heads, int32_t max_blocks);

@@ -235,7 +235,10 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
  *   q_idx        : [n_layers][batch][Di] bf16
  *   q            : [n_layers][batch][H][D] bf16
  *   block_scores : [n_layers][batch][max_blocks] float32, written
- *   block_idx    : [n_layers][batch][topk_blocks] int32, written
+ *   block_idx    : [n_layers][batch][topk_blocks] int32, written (a one
+ *                  launch below 2048 blocks first fills it with INT32_MIN,
+ *                  which its attention items poll for, and then overwrites
+ *                  every entry; other workgroups read it during the call)
  *   n_sel        : [n_layers][batch] int32 or NULL
  *   out          : [n_layers][batch][H][D] float32, written
  *   lse          : [n_layers][batch][H] float32 or NULL
