@@ -32,9 +32,12 @@
 // completion counter.  A reader polls the counter, then takes a device-scope
 // acquire fence (an L1/L2 invalidation of its XCD) before reading, so it
 // cannot hit a stale line; the layer-order wait of a scoring item reads
-// nothing the launch produced and takes no fence.  No L2 write-back is
-// needed on the writer's side.  A clear kernel zeroes the counters before
-// each launch.
+// nothing the launch produced and takes no fence.  Below 2048 blocks an
+// attention item instead polls the published ids themselves with
+// device-scope loads (the id output is filled with a pending marker before
+// the launch), which needs neither the counter nor the fence.  No L2
+// write-back is needed on the writer's side.  A clear kernel zeroes the
+// counters (and writes the markers) before each launch.
 #include <mutex>
 
 #include "attn_common.h"
