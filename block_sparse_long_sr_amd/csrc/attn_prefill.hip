@@ -503,10 +503,17 @@ __global__ __launch_bounds__(kBlockWaves * kWave) void attn_prefill_local_kernel
   const WsView w = ws_view(a);
   const int wave = wave_id();
   const int lw = a.plan.local_win;
-  const int64_t unit = (int64_t)blockIdx.x * kBlockWaves + wave;
-  const int rb = (int)(unit / A.heads);
-  const int h = (int)(unit - (int64_t)rb * A.heads);
-  if (rb >= row_blocks(A)) return;
+  // XCD-aware order: workgroup g runs on XCD g % 8.  Each XCD takes a
+  // contiguous range of row blocks for every head, head-major, so the waves
+  // of a workgroup and its neighbours on the XCD are consecutive row blocks
+  // of one head, which share lw - 1 of their lw window tiles through that
+  // XCD's L2 instead of each XCD fetching them from memory again.
+  const int nrb = row_blocks(A);
+  const int per_xcd = (nrb + 7) >> 3;
+  const int64_t u = (int64_t)(blockIdx.x >> 3) * kBlockWaves + wave;  // unit within the XCD
+  const int h = (int)(u / per_xcd);
+  const int rb = (int)(blockIdx.x & 7) * per_xcd + (int)(u - (int64_t)h * per_xcd);
+  if (h >= A.heads || rb >= nrb) return;
   const int bp = (A.q_start >> 5) + rb;
   const int t0 = max(0, bp * kBlock - A.q_start);
   const int nrows = min(A.nq, (bp + 1) * kBlock - A.q_start) - t0;  // 1 .. 32
@@ -821,8 +828,11 @@ SideStream* side_stream() {
 hipError_t launch_attn_prefill_blocks(const PrefillAttnArgs& a, hipStream_t stream) {
   const AttnArgs& A = a.attn;
   if (A.nq == 0) return hipSuccess;
+  // window pass: 8 XCDs x the workgroups of one XCD's row-block range for
+  // every head (see attn_prefill_local_kernel)
   const int64_t lunits = a.plan.local_win > 0 ? (int64_t)row_blocks_host(A) * A.heads : 0;
-  const dim3 lgrid((unsigned)((lunits + kBlockWaves - 1) / kBlockWaves));
+  const int64_t lunits_xcd = (int64_t)((row_blocks_host(A) + 7) / 8) * A.heads;
+  const dim3 lgrid((unsigned)(8 * ((lunits_xcd + kBlockWaves - 1) / kBlockWaves)));
   SideStream* side = lunits > 0 ? side_stream() : nullptr;
   std::unique_lock<std::mutex> lock;
   if (side != nullptr) {
