@@ -303,16 +303,25 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
 DecodeStepPlan decode_step_plan(int32_t n_layers, int32_t batch, int32_t heads, int32_t max_blocks) {
   DecodeStepPlan p{};
   const int64_t S = (int64_t)n_layers * batch;
+  // Blocks per scoring item: 32 (256 KB of indexer keys) at long contexts
+  // and for batches of at least 16384 blocks, where an item's fixed cost
+  // (its layer-order poll, the store drain and the completion count, one
+  // memory round trip each) is worth spreading over more bytes; 16 for
+  // smaller batches, so that a sequence's scoring spreads over many
+  // workgroups and finishes soon after its first item starts (us per step,
+  // 12 layers, one workgroup per CU, chunk 16 / 32 at the lag below:
+  // 16 x 32K 410-414 / 399; 16 x 48K 548 / 494; 32 x 32K 766 / 700;
+  // 16 x 16K 344 / 368; 8 x 32K 296 / 329; 16 x 8K 313 / 336).
+  const int64_t batch_blocks = (int64_t)batch * max_blocks;
+  p.chunk = (max_blocks >= 2048 || batch_blocks >= 16384) ? kMaxStepChunk : 16;
   // Slots between a slot's scoring items and its attention items: long
   // enough for the slot's scoring and selection to finish, short enough for
   // its attention to finish before the sequence's next layer comes up, which
   // is batch slots later.  Half the batch (below batch, as the ticket order
-  // requires); measured best at 16 sequences x 128K.
-  p.lag = batch / 2;
-  // Blocks per scoring item: 32 (256 KB of indexer keys) at long contexts,
-  // 16 below 2048 blocks, so that a sequence's scoring spreads over many
-  // workgroups and finishes soon after its first item starts.
-  p.chunk = max_blocks >= 2048 ? kMaxStepChunk : 16;
+  // requires), measured best at 16 sequences x 128K and 48K; three eighths
+  // with 32-block items up to 1024 blocks, whose scoring finishes sooner
+  // (16 x 32K: lag 6 399 us, 8 408 us; 32 x 32K: lag 12 700 us, 16 705 us).
+  p.lag = (p.chunk == kMaxStepChunk && max_blocks <= 1024) ? (3 * batch) / 8 : batch / 2;
   // Workgroups per CU: two at long contexts; one below 2048 blocks, where a
   // sequence's layer chain (scoring, selection, attention) rather than
   // bandwidth sets the pace and half the bytes in flight shorten the memory
