@@ -253,7 +253,8 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
  *                  share a workspace must be stream-ordered.
  * Requires topk_blocks <= 256, max_blocks - local_blocks <= 16384 and
  * n_layers * batch * (ceil(max_blocks / chunk) + H) < 2^31 work items
- * (chunk = 32 blocks per scoring item from max_blocks 2048 up, 16 below);
+ * (chunk = 32 blocks per scoring item from max_blocks 2048 up and when
+ * batch * max_blocks >= 16384, 16 otherwise);
  * UOCR_EUNSUPPORTED otherwise.  UOCR_EWORKSPACE when ws is NULL or too
  * small, UOCR_EINVAL when it is not 256-byte aligned or schedule is not one
  * of the three values.
