@@ -93,7 +93,7 @@ __device__ __forceinline__ void reduce_key_groups(float& l, float (&o)[8]) {
   }
 }
 
-// LDS of attend_query_wg: one online-softmax state per wave.
+// LDS of wave_attn_finish: one online-softmax state per wave.
 template <int NT>
 struct AttendSmem {
   float m[NT / kWave];
@@ -101,53 +101,71 @@ struct AttendSmem {
   float o[NT / kWave][kDim];
 };
 
-// Attention of one query head at position p over the kept blocks
-// sel[0 .. topk) (global or LDS memory; -1 and out-of-range entries, blocks
-// starting after p and blocks whose pool index is out of range are
-// skipped).  The blocks are split over the NT/64 waves of the workgroup
-// (split-K), whose states are merged through LDS; every thread calls it.
-// kStream as for load_block_tiles.
-//   k_pool, v_pool : [num_blocks][heads][32][128] bf16;  table : the
-//   sequence's block-table row;  q_head : the head's 128 query dims;
-//   out_head : 128 floats;  lse_out : one float or null (natural log).
+// One wave's online-softmax state of a query head: m (running max, log2
+// units, wave-uniform), l (running sum over the lane's key group), o (the
+// lane's 8-dim slice of the unnormalised output) and the lane's query slice.
+struct WaveAttn {
+  float m;
+  float l;
+  float o[8];
+  uint4 qv;
+};
+
+__device__ __forceinline__ void wave_attn_init(WaveAttn& st, const uint16_t* q_head) {
+  st.qv = *reinterpret_cast<const uint4*>(q_head + (lane_id() & 15) * 8);
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) st.o[d] = 0.0f;
+}
+
+// Block j of the sequence (table: its block-table row) into the wave's
+// state; blocks starting after p and out-of-range pool indices are skipped.
+template <bool kStream>
+__device__ __forceinline__ void wave_attn_block(const uint16_t* k_pool, const uint16_t* v_pool, const int32_t* table,
+                                                int64_t num_blocks, int heads, int h, int j, int p, float scale_log2,
+                                                WaveAttn& st) {
+  if (j * kBlock > p) return;
+  const int pb = __builtin_amdgcn_readfirstlane(table[j]);
+  if (pb < 0 || (int64_t)pb >= num_blocks) return;
+  const int64_t tile = ((int64_t)pb * heads + h) * (kBlock * kDim);
+  attend_block<kStream>(k_pool + tile, v_pool + tile, j, p, st.qv, scale_log2, st.m, st.l, st.o);
+}
+
+// Entries e = wave, wave + NW, ... of sel[0 .. topk) into the wave's state;
+// -1 entries and ids outside [0, j_end) are skipped (j_end = max_blocks for
+// all of them; a smaller j_end leaves out blocks already attended).
 template <int NT, bool kStream>
-__device__ __forceinline__ void attend_query_wg(const uint16_t* k_pool, const uint16_t* v_pool, const int32_t* table,
-                                                int64_t num_blocks, int heads, int h, int max_blocks, int p,
-                                                const uint16_t* q_head, const int32_t* sel, int topk,
-                                                float scale_log2, float* out_head, float* lse_out,
-                                                AttendSmem<NT>& sm) {
+__device__ __forceinline__ void wave_attn_sel(const uint16_t* k_pool, const uint16_t* v_pool, const int32_t* table,
+                                              int64_t num_blocks, int heads, int h, int j_end, int p,
+                                              const int32_t* sel, int topk, float scale_log2, WaveAttn& st) {
+  constexpr int NW = NT / kWave;
+  for (int e = wave_id(); e < topk; e += NW) {
+    const int j = __builtin_amdgcn_readfirstlane(sel[e]);
+    if (j < 0 || j >= j_end) continue;
+    wave_attn_block<kStream>(k_pool, v_pool, table, num_blocks, heads, h, j, p, scale_log2, st);
+  }
+}
+
+// The workgroup's NT/64 wave states merged through LDS into the head's
+// normalised output (128 floats) and its lse (natural log; lse_out may be
+// null); every thread calls it.
+template <int NT>
+__device__ __forceinline__ void wave_attn_finish(WaveAttn& st, float* out_head, float* lse_out, AttendSmem<NT>& sm) {
   constexpr int NW = NT / kWave;
   const int lane = lane_id();
   const int wave = wave_id();
-  const int c8 = (lane & 15) * 8;  // first dim of the lane's slice
-  const uint4 qv = *reinterpret_cast<const uint4*>(q_head + c8);
-
-  float m = -INFINITY;  // running max (log2 units), wave-uniform
-  float l = 0.0f;       // running sum over this lane's key group
-  float o[8];
-#pragma unroll
-  for (int d = 0; d < 8; ++d) o[d] = 0.0f;
-
-  for (int e = wave; e < topk; e += NW) {
-    const int j = __builtin_amdgcn_readfirstlane(sel[e]);
-    if (j < 0 || j >= max_blocks || j * kBlock > p) continue;
-    const int pb = __builtin_amdgcn_readfirstlane(table[j]);
-    if (pb < 0 || (int64_t)pb >= num_blocks) continue;
-    const int64_t tile = ((int64_t)pb * heads + h) * (kBlock * kDim);
-    attend_block<kStream>(k_pool + tile, v_pool + tile, j, p, qv, scale_log2, m, l, o);
-  }
-
-  reduce_key_groups(l, o);
+  const int c8 = (lane & 15) * 8;
+  reduce_key_groups(st.l, st.o);
   if (lane == 0) {
-    sm.m[wave] = m;
-    sm.l[wave] = l;
+    sm.m[wave] = st.m;
+    sm.l[wave] = st.l;
   }
   if (lane < 16) {
 #pragma unroll
-    for (int d = 0; d < 8; ++d) sm.o[wave][c8 + d] = o[d];
+    for (int d = 0; d < 8; ++d) sm.o[wave][c8 + d] = st.o[d];
   }
   __syncthreads();
-
   if (threadIdx.x < kDim) {
     const int d = threadIdx.x;
     float M = -INFINITY;
@@ -168,6 +186,27 @@ __device__ __forceinline__ void attend_query_wg(const uint16_t* k_pool, const ui
     out_head[d] = res;
     if (lse_out != nullptr && d == 0) *lse_out = lse_v;
   }
+}
+
+// Attention of one query head at position p over the kept blocks
+// sel[0 .. topk) (global or LDS memory; -1 and out-of-range entries, blocks
+// starting after p and blocks whose pool index is out of range are
+// skipped).  The blocks are split over the NT/64 waves of the workgroup
+// (split-K), whose states are merged through LDS; every thread calls it.
+// kStream as for load_block_tiles.
+//   k_pool, v_pool : [num_blocks][heads][32][128] bf16;  table : the
+//   sequence's block-table row;  q_head : the head's 128 query dims;
+//   out_head : 128 floats;  lse_out : one float or null (natural log).
+template <int NT, bool kStream>
+__device__ __forceinline__ void attend_query_wg(const uint16_t* k_pool, const uint16_t* v_pool, const int32_t* table,
+                                                int64_t num_blocks, int heads, int h, int max_blocks, int p,
+                                                const uint16_t* q_head, const int32_t* sel, int topk,
+                                                float scale_log2, float* out_head, float* lse_out,
+                                                AttendSmem<NT>& sm) {
+  WaveAttn st;
+  wave_attn_init(st, q_head);
+  wave_attn_sel<NT, kStream>(k_pool, v_pool, table, num_blocks, heads, h, max_blocks, p, sel, topk, scale_log2, st);
+  wave_attn_finish<NT>(st, out_head, lse_out, sm);
 }
 
 }  // namespace uocr

@@ -12,7 +12,8 @@
 //     workgroup that completes the last chunk of (l, b) then runs the
 //     selection of (l, b) once and publishes the kept block ids;
 //   * attention item (l, b, head h): the attention of head h over the
-//     published selection.
+//     published selection; its local-window blocks, kept whatever the
+//     ranking, are attended while the selection is awaited.
 // "Slot" s = l * batch + b.  The ticket order is: the scoring items of slot
 // s, then the attention items of slot s - lag, for s = 0, 1, ...; the last
 // `lag` slots' attention items close the list.  With lag < batch, each item
@@ -266,8 +267,21 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
         if (tid == 0) count_done(sel_done + it.slot);
       }
     } else {
-      // the sequence's table row goes to LDS while the selection is awaited,
-      // so the kept ids are followed by one memory round trip (the tiles)
+      const int h = it.idx;
+      const int64_t head_row = (int64_t)it.slot * H + h;
+      const int64_t kv_off = (int64_t)l * a.kv_layer_stride;
+      const uint16_t* kp = a.k_pool + kv_off;
+      const uint16_t* vp = a.v_pool + kv_off;
+      // The local window (blocks ncand .. nb - 1) is kept whatever the
+      // ranking: the last waves attend it while the selection is awaited, so
+      // only the remote blocks' tiles follow the kept ids (16 x 12 x 32K:
+      // 400 -> 387-392 us; 128K within its spread, 1084 -> 1080-1083 us).
+      WaveAttn st;
+      wave_attn_init(st, a.q + head_row * kDim);
+      for (int i = kStepWaves - 1 - wave; i < nb - ncand; i += kStepWaves)
+        wave_attn_block<true>(kp, vp, table, a.num_blocks, H, h, ncand + i, L - 1, a.scale_log2, st);
+      // the sequence's table row goes to LDS meanwhile, so the kept ids are
+      // followed by one memory round trip (the tiles)
       const bool cached = M <= kTableCache;
       if (cached)
         for (int i = tid; i < M; i += kStepThreads) s_table[i] = table[i];
@@ -281,14 +295,11 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
         for (int i = tid; i < a.topk; i += kStepThreads) s_blocks[i] = sel_out[i];
       }
       __syncthreads();
-      const int h = it.idx;
-      const int64_t head_row = (int64_t)it.slot * H + h;
-      const int64_t kv_off = (int64_t)l * a.kv_layer_stride;
-      attend_query_wg<kStepThreads, true>(a.k_pool + kv_off, a.v_pool + kv_off, cached ? s_table : table,
-                                          a.num_blocks, H, h, M,
-                                          L - 1, a.q + head_row * kDim, s_blocks, a.topk, a.scale_log2,
-                                          a.out + head_row * kDim, a.lse != nullptr ? a.lse + head_row : nullptr,
-                                          att_sm);
+      // the remote blocks: every kept id below ncand
+      wave_attn_sel<kStepThreads, true>(kp, vp, cached ? s_table : table, a.num_blocks, H, h, ncand, L - 1,
+                                        s_blocks, a.topk, a.scale_log2, st);
+      wave_attn_finish<kStepThreads>(st, a.out + head_row * kDim, a.lse != nullptr ? a.lse + head_row : nullptr,
+                                     att_sm);
       if (tid == 0) next_t = take_ticket(ticket);
       drain_stores();
       __syncthreads();
