@@ -147,6 +147,40 @@ __device__ __forceinline__ void wave_attn_sel(const uint16_t* k_pool, const uint
   }
 }
 
+// As wave_attn_sel, with the tiles of the wave's entries e and e + NW
+// loaded together before either is attended (two blocks' K and V in flight:
+// 128 VGPRs of tiles, for kernels with 256 VGPRs per wave); the blocks are
+// attended in the same order, so the result is the same.
+template <int NT, bool kStream>
+__device__ __forceinline__ void wave_attn_sel_pairs(const uint16_t* k_pool, const uint16_t* v_pool,
+                                                    const int32_t* table, int64_t num_blocks, int heads, int h,
+                                                    int j_end, int p, const int32_t* sel, int topk, float scale_log2,
+                                                    WaveAttn& st) {
+  constexpr int NW = NT / kWave;
+  for (int e = wave_id(); e < topk; e += 2 * NW) {
+    const int e2 = e + NW;
+    const int ja = __builtin_amdgcn_readfirstlane(sel[e]);
+    const int jb = e2 < topk ? __builtin_amdgcn_readfirstlane(sel[e2]) : -1;
+    bool oka = ja >= 0 && ja < j_end && ja * kBlock <= p;
+    bool okb = jb >= 0 && jb < j_end && jb * kBlock <= p;
+    const int pba = oka ? __builtin_amdgcn_readfirstlane(table[ja]) : -1;
+    const int pbb = okb ? __builtin_amdgcn_readfirstlane(table[jb]) : -1;
+    oka = oka && pba >= 0 && (int64_t)pba < num_blocks;
+    okb = okb && pbb >= 0 && (int64_t)pbb < num_blocks;
+    uint4 ka[8], va[8], kb[8], vb[8];
+    if (oka) {
+      const int64_t tile = ((int64_t)pba * heads + h) * (kBlock * kDim);
+      load_block_tiles<kStream>(k_pool + tile, v_pool + tile, ka, va);
+    }
+    if (okb) {
+      const int64_t tile = ((int64_t)pbb * heads + h) * (kBlock * kDim);
+      load_block_tiles<kStream>(k_pool + tile, v_pool + tile, kb, vb);
+    }
+    if (oka) attend_loaded_block(ka, va, ja, p, st.qv, scale_log2, st.m, st.l, st.o);
+    if (okb) attend_loaded_block(kb, vb, jb, p, st.qv, scale_log2, st.m, st.l, st.o);
+  }
+}
+
 // The workgroup's NT/64 wave states merged through LDS into the head's
 // normalised output (128 floats) and its lse (natural log; lse_out may be
 // null); every thread calls it.

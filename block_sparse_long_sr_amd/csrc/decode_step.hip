@@ -164,8 +164,11 @@ __global__ __launch_bounds__(kStepThreads) void decode_step_clear_kernel(uint32_
   if (status_out != nullptr && threadIdx.x == 0) *status_out = 0;
 }
 
-template <int KPT>
-__global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_step_kernel(
+// WIDE: the launch keeps one workgroup per compute unit (contexts below 2048
+// blocks), so a wave may use 256 VGPRs, and an attention item's wave loads
+// the tiles of both its remote blocks before attending either.
+template <int KPT, bool WIDE>
+__global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(WIDE ? 2 : 4))) void decode_step_kernel(
     DecodeStepArgs a) {
   __shared__ SelectSmem<kStepThreads> sel_sm;
   __shared__ AttendSmem<kStepThreads> att_sm;
@@ -296,8 +299,12 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(4)
       }
       __syncthreads();
       // the remote blocks: every kept id below ncand
-      wave_attn_sel<kStepThreads, true>(kp, vp, cached ? s_table : table, a.num_blocks, H, h, ncand, L - 1,
-                                        s_blocks, a.topk, a.scale_log2, st);
+      if (WIDE)
+        wave_attn_sel_pairs<kStepThreads, true>(kp, vp, cached ? s_table : table, a.num_blocks, H, h, ncand, L - 1,
+                                                s_blocks, a.topk, a.scale_log2, st);
+      else
+        wave_attn_sel<kStepThreads, true>(kp, vp, cached ? s_table : table, a.num_blocks, H, h, ncand, L - 1,
+                                          s_blocks, a.topk, a.scale_log2, st);
       wave_attn_finish<kStepThreads>(st, a.out + head_row * kDim, a.lse != nullptr ? a.lse + head_row : nullptr,
                                      att_sm);
       if (tid == 0) next_t = take_ticket(ticket);
@@ -361,7 +368,7 @@ static_assert(sizeof(SelectSmem<kStepThreads>) + sizeof(AttendSmem<kStepThreads>
                   160 * 1024 / 2,
               "two step workgroups must fit in one CU's LDS");
 
-template <int KPT>
+template <int KPT, bool WIDE>
 hipError_t launch_step(const DecodeStepArgs& a, const DecodeStepPlan& plan, hipStream_t stream) {
   // One resident wave of workgroups (they loop over the tickets).  A grid
   // larger than what fits is also correct: a workgroup takes a ticket only
@@ -373,7 +380,7 @@ hipError_t launch_step(const DecodeStepArgs& a, const DecodeStepPlan& plan, hipS
   if (e != hipSuccess) return e;
   const int64_t fit = (int64_t)plan.groups_per_cu * (cus > 0 ? cus : 1);
   const int64_t grid = plan.items < fit ? plan.items : fit;
-  hipLaunchKernelGGL(decode_step_kernel<KPT>, dim3((unsigned)grid), dim3(kStepThreads), 0, stream, a);
+  hipLaunchKernelGGL((decode_step_kernel<KPT, WIDE>), dim3((unsigned)grid), dim3(kStepThreads), 0, stream, a);
   return hipGetLastError();
 }
 }  // namespace
@@ -487,8 +494,11 @@ hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& pla
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t max_cand = (int64_t)a.max_blocks - a.local_blocks;
-  if (max_cand <= kStepThreads * 8) return launch_step<8>(a, plan, stream);
-  if (max_cand <= kStepThreads * 32) return launch_step<32>(a, plan, stream);
+  if (max_cand <= kStepThreads * 8) {
+    if (plan.groups_per_cu == 1) return launch_step<8, true>(a, plan, stream);
+    return launch_step<8, false>(a, plan, stream);
+  }
+  if (max_cand <= kStepThreads * 32) return launch_step<32, false>(a, plan, stream);
   return hipErrorInvalidValue;
 }
 
