@@ -332,20 +332,22 @@ DecodeStepPlan decode_step_plan(int32_t n_layers, int32_t batch, int32_t heads, 
   // 16 x 16K 344 / 368; 8 x 32K 296 / 329; 16 x 8K 313 / 336).
   const int64_t batch_blocks = (int64_t)batch * max_blocks;
   p.chunk = (max_blocks >= 2048 || batch_blocks >= 16384) ? kMaxStepChunk : 16;
-  // Slots between a slot's scoring items and its attention items: long
-  // enough for the slot's scoring and selection to finish, short enough for
-  // its attention to finish before the sequence's next layer comes up, which
-  // is batch slots later.  Half the batch (below batch, as the ticket order
-  // requires), measured best at 16 sequences x 128K and 48K; three eighths
-  // with 32-block items up to 1024 blocks, whose scoring finishes sooner
-  // (16 x 32K: lag 6 399 us, 8 408 us; 32 x 32K: lag 12 700 us, 16 705 us).
-  p.lag = (p.chunk == kMaxStepChunk && max_blocks <= 1024) ? (3 * batch) / 8 : batch / 2;
   // Workgroups per CU: two at long contexts; one below 2048 blocks, where a
   // sequence's layer chain (scoring, selection, attention) rather than
   // bandwidth sets the pace and half the bytes in flight shorten the memory
   // latency every step of the chain sees (16 x 12 x 32K: 447-464 us against
   // 598 us with two; at 128K two are better, 1103 against 1138 us).
   p.groups_per_cu = max_blocks >= 2048 ? 2 : 1;
+  // Slots between a slot's scoring items and its attention items: long
+  // enough for the slot's scoring and selection to finish, short enough for
+  // its attention to finish before the sequence's next layer comes up, which
+  // is batch slots later (below batch, as the ticket order requires).  Half
+  // the batch with two workgroups per CU (16 x 128K: lag 8 1082, 6 1080 us);
+  // three eighths with one, whose attention items attend their local window
+  // while the selection is awaited and so may arrive earlier (us per step at
+  // lag 3B/8 / B/2: 16 x 32K 378 / 395; 16 x 16K 335 / 349; 16 x 48K 487 /
+  // 488; 32 x 32K 714 / 714).
+  p.lag = p.groups_per_cu == 1 ? (3 * batch) / 8 : batch / 2;
   // Attention items poll the published ids directly (the id output is
   // filled with kSelPending before the launch) where the layer chain sets
   // the pace: one memory round trip less per layer (16 x 12 x 32K: 398-406
