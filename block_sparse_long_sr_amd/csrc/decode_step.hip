@@ -422,15 +422,18 @@ bool decode_step_one_launch(int32_t n_layers, int32_t batch, int32_t max_blocks)
   // a sequence must be scored, selected and attended within the time the
   // other sequences' scoring of that layer takes, about batch * max_blocks *
   // 8 KB at HBM rate, and the first and last layers run with little to
-  // overlap.  Measured (us per step, one launch against per-layer launches,
-  // 12 layers): 16 sequences at 16K 375/332, 24K 397/400, 32K 443/468, 64K
-  // 715/713, 96K 868/959; 8 at 64K 512/447, 8 at 128K 680/716; 4 at 128K
-  // 486/450; 32 at 16K 531/550; 64 at 4K 528/560; 16 x 32K with 2 and 4
-  // layers 96/78 and 162/155.  Hence: at least 8 layers, and enough blocks
-  // in the batch for the sequence's size.
+  // overlap.  Measured (us per step, one launch / per-layer launches, 12
+  // layers unless stated): below 2048 blocks (one workgroup per CU) 16 x 4K
+  // 261/231, 16 x 8K 296/269, 16 x 16K 327/331, 16 x 24K 355/398, 4 x 32K
+  // 256/250, 8 x 32K 286/327, 32 x 8K 392/433, 64 x 4K 515/582, 32 x 16K
+  // 459/552, 16 x 32K with 2, 4 and 8 layers 83/76, 142/151, 257/299; from
+  // 2048 blocks (two per CU) 8 x 64K 486/455, 4 x 128K 435/442, 16 x 64K
+  // 668/703, 8 x 128K 617/701.  Hence: at least 4 layers, and a batch of
+  // at least 8192 blocks and 8 sequences below 2048 blocks, of at least
+  // 32768 blocks from there.
   const int64_t blocks = (int64_t)batch * max_blocks;
-  return n_layers >= 8 &&
-         (blocks >= 32768 || (batch >= 16 && blocks >= 16384) || (batch >= 32 && blocks >= 8192));
+  if (n_layers < 4) return false;
+  return max_blocks < 2048 ? (batch >= 8 && blocks >= 8192) : blocks >= 32768;
 }
 
 hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& plan, bool one_launch,

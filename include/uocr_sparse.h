@@ -223,11 +223,11 @@ int uocr_topk_attn_decode(const uocr_sparse_cfg* cfg, const uocr_kv* kv, const u
  *     launches below.
  *   UOCR_STEP_PER_LAYER: per layer, the scoring launch and the fused
  *     selection + attention launch of uocr_topk_attn_decode.
- *   UOCR_STEP_AUTO: the one launch when n_layers >= 8 and batch *
- *     max_blocks >= 32768, or >= 16384 with batch >= 16, or >= 8192 with
- *     batch >= 32 (the one launch needs enough other sequences' scoring to
- *     hide each sequence's layer-to-layer latency, and enough layers to
- *     amortise its start and end), otherwise per layer.
+ *   UOCR_STEP_AUTO: the one launch when n_layers >= 4 and either
+ *     max_blocks < 2048, batch >= 8 and batch * max_blocks >= 8192, or
+ *     batch * max_blocks >= 32768 (the one launch needs enough other
+ *     sequences' scoring to hide each sequence's layer-to-layer latency, and
+ *     enough layers to amortise its start and end), otherwise per layer.
  * kv describes layer 0 and holds every layer, layer-major:
  *   kv->k_pool, kv->v_pool : [n_layers][num_blocks][H][32][D] bf16
  *   kv->kidx_pool          : [n_layers][num_blocks][32][Di] bf16
