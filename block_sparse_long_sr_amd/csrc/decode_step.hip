@@ -212,62 +212,72 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(WI
       const int j0 = it.idx * chunk;
       const int jend_all = min(j0 + chunk, M);
       const int jend = min(jend_all, ncand);
-      // the pool indices of the wave's first two blocks are read before the
-      // wait for the previous layer (the table does not depend on it)
-      const int jA = j0 + wave, jB = jA + kStepWaves;
-      const int pbA = jA < jend ? __builtin_amdgcn_readfirstlane(table[jA]) : -1;
-      const int pbB = jB < jend ? __builtin_amdgcn_readfirstlane(table[jB]) : -1;
-      if (l > 0) {
-        if (tid == 0) wait_count<false>(attn_done + (it.slot - B), (uint32_t)H, err, a.status_out);
-        __syncthreads();
-      }
-      if (j0 < jend) {
-        const uint4 qv = *reinterpret_cast<const uint4*>(a.q_idx + (int64_t)it.slot * kDim + (lane & 15) * 8);
-        const uint16_t* kidx = a.kidx_pool + (int64_t)l * a.kidx_layer_stride;
-        // blocks j and j + kStepWaves of the wave are loaded together
-        for (int j = jA; j < jend; j += 2 * kStepWaves) {
-          const int j2 = j + kStepWaves;
-          const int pb = j == jA ? pbA : __builtin_amdgcn_readfirstlane(table[j]);
-          const int pb2 = j == jA ? pbB : (j2 < jend ? __builtin_amdgcn_readfirstlane(table[j2]) : -1);
-          const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
-          const bool ok2 = pb2 >= 0 && (int64_t)pb2 < a.num_blocks;
-          uint4 kv[8], kv2[8];
-          load_index_tile(kidx + (int64_t)(ok ? pb : 0) * (kBlock * kDim), kv);
-          load_index_tile(kidx + (int64_t)(ok2 ? pb2 : 0) * (kBlock * kDim), kv2);
-          const float s1 = ok ? block_max_of_tile(kv, qv) : __builtin_nanf("");
-          const float s2 = ok2 ? block_max_of_tile(kv2, qv) : __builtin_nanf("");
-          if (lane == 0) {
-            s_chunk[j - j0] = s1;
-            if (j2 < jend) s_chunk[j2 - j0] = s2;
+      // Chunks past the sequence's candidates (ragged batches) hold only -inf
+      // scores, which nothing in the launch reads: such an item skips the
+      // layer-order wait, the publication and the count, and the slot's
+      // selection waits for its cb candidate chunks only.
+      const int cb = ncand > 0 ? (ncand + chunk - 1) / chunk : 1;
+      if (it.idx >= cb) {
+        for (int j = j0 + tid; j < jend_all; j += kStepThreads) scores[j] = -INFINITY;
+        if (tid == 0) next_t = take_ticket(ticket);
+      } else {
+        // the pool indices of the wave's first two blocks are read before the
+        // wait for the previous layer (the table does not depend on it)
+        const int jA = j0 + wave, jB = jA + kStepWaves;
+        const int pbA = jA < jend ? __builtin_amdgcn_readfirstlane(table[jA]) : -1;
+        const int pbB = jB < jend ? __builtin_amdgcn_readfirstlane(table[jB]) : -1;
+        if (l > 0) {
+          if (tid == 0) wait_count<false>(attn_done + (it.slot - B), (uint32_t)H, err, a.status_out);
+          __syncthreads();
+        }
+        if (j0 < jend) {
+          const uint4 qv = *reinterpret_cast<const uint4*>(a.q_idx + (int64_t)it.slot * kDim + (lane & 15) * 8);
+          const uint16_t* kidx = a.kidx_pool + (int64_t)l * a.kidx_layer_stride;
+          // blocks j and j + kStepWaves of the wave are loaded together
+          for (int j = jA; j < jend; j += 2 * kStepWaves) {
+            const int j2 = j + kStepWaves;
+            const int pb = j == jA ? pbA : __builtin_amdgcn_readfirstlane(table[j]);
+            const int pb2 = j == jA ? pbB : (j2 < jend ? __builtin_amdgcn_readfirstlane(table[j2]) : -1);
+            const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
+            const bool ok2 = pb2 >= 0 && (int64_t)pb2 < a.num_blocks;
+            uint4 kv[8], kv2[8];
+            load_index_tile(kidx + (int64_t)(ok ? pb : 0) * (kBlock * kDim), kv);
+            load_index_tile(kidx + (int64_t)(ok2 ? pb2 : 0) * (kBlock * kDim), kv2);
+            const float s1 = ok ? block_max_of_tile(kv, qv) : __builtin_nanf("");
+            const float s2 = ok2 ? block_max_of_tile(kv2, qv) : __builtin_nanf("");
+            if (lane == 0) {
+              s_chunk[j - j0] = s1;
+              if (j2 < jend) s_chunk[j2 - j0] = s2;
+            }
           }
         }
-      }
-      __syncthreads();
-      // one coalesced store of the item's scores (non-candidates: -inf)
-      for (int j = j0 + tid; j < jend_all; j += kStepThreads)
-        publish(scores + j, j < jend ? s_chunk[j - j0] : -INFINITY);
-      if (tid == 0) next_t = take_ticket(ticket);
-      drain_stores();
-      __syncthreads();
-      if (tid == 0) {
-        const bool last = count_done(score_done + it.slot) == (uint32_t)(C - 1);
-        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every chunk's scores are visible
-        s_last = last;
-      }
-      __syncthreads();
-      if (s_last) {
-        // the slot's scoring is complete: select once for its heads
-        const int R = a.topk - a.local_blocks;
-        if (!select_trivial(nb, ncand, R, a.topk, s_blocks, kStepThreads))
-          select_sorted_reg<kStepThreads, KPT>(scores, ncand, R, a.local_blocks, s_blocks, sel_sm,
-                                               a.block_page != nullptr ? a.block_page + (int64_t)b * M : nullptr,
-                                               a.block_page != nullptr ? a.query_page[b] : 0);
         __syncthreads();
-        for (int i = tid; i < a.topk; i += kStepThreads) publish(sel_out + i, s_blocks[i]);
-        if (a.n_sel != nullptr && tid == 0) a.n_sel[it.slot] = nb < a.topk ? nb : a.topk;
+        // one coalesced store of the item's scores (non-candidates: -inf)
+        for (int j = j0 + tid; j < jend_all; j += kStepThreads)
+          publish(scores + j, j < jend ? s_chunk[j - j0] : -INFINITY);
+        if (tid == 0) next_t = take_ticket(ticket);
         drain_stores();
         __syncthreads();
-        if (tid == 0) count_done(sel_done + it.slot);
+        if (tid == 0) {
+          const bool last = count_done(score_done + it.slot) == (uint32_t)(cb - 1);
+          if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every chunk's scores are visible
+          s_last = last;
+        }
+        __syncthreads();
+        if (s_last) {
+          // the slot's scoring is complete: select once for its heads
+          const int R = a.topk - a.local_blocks;
+          if (!select_trivial(nb, ncand, R, a.topk, s_blocks, kStepThreads))
+            select_sorted_reg<kStepThreads, KPT>(scores, ncand, R, a.local_blocks, s_blocks, sel_sm,
+                                                 a.block_page != nullptr ? a.block_page + (int64_t)b * M : nullptr,
+                                                 a.block_page != nullptr ? a.query_page[b] : 0);
+          __syncthreads();
+          for (int i = tid; i < a.topk; i += kStepThreads) publish(sel_out + i, s_blocks[i]);
+          if (a.n_sel != nullptr && tid == 0) a.n_sel[it.slot] = nb < a.topk ? nb : a.topk;
+          drain_stores();
+          __syncthreads();
+          if (tid == 0) count_done(sel_done + it.slot);
+        }
       }
     } else {
       const int h = it.idx;
