@@ -577,11 +577,20 @@ def run_page_gate(U, SD, W, torch, reps=20):
     t1_gate = timed(lambda: lib_step(kv_gate, U.STEP_ONE_LAUNCH))
     ta_plain = timed(lambda: lib_step(kv_plain, U.STEP_AUTO))
     ta_gate = timed(lambda: lib_step(kv_gate, U.STEP_AUTO))
+    # per-layer launches over two micro-batches of 32 documents on two
+    # streams of the caller's, forked and joined once around the repeated
+    # steps: each half's next step depends only on its own previous one, as
+    # in a decode loop, so the halves run as two pipelines
+    st2, fk, jn = micro_batch_step(U, torch, dev, cfg,
+                                   (scores1, idx.view(1, B, 16), out.view(1, B, H, 128), lse.view(1, B, H)), 2)
+    t2_plain = time_steps(torch, stream, st2, reps, 3, fk, jn)
     idx_b, topk_b, attn_b = decode_bytes(wl)
     step_bytes = idx_b + topk_b + attn_b
     us = {"plain": t_plain, "page_aware": t_gate, "one_launch_plain": t1_plain, "one_launch_page_aware": t1_gate,
-          "auto_plain": ta_plain, "auto_page_aware": ta_gate}
+          "auto_plain": ta_plain, "auto_page_aware": ta_gate, "two_streams_plain": t2_plain}
     res["decode"] = {"workload": wl.name, "queries": B, "algorithmic_bytes": step_bytes,
+                     "two_streams_note": "two micro-batches of 32 documents on two streams, joined once around "
+                                         "the repeated steps (two independent pipelines, as in a decode loop)",
                      "us": {k: v * 1e3 for k, v in us.items()},
                      "query_heads_per_s": {k: B * H / (v * 1e-3) for k, v in us.items()},
                      "hbm_frac": {k: step_bytes / (v * 1e-3) / 1e9 / HBM_PEAK_GBPS for k, v in us.items()}}
