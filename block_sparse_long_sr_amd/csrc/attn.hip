@@ -19,8 +19,9 @@ namespace uocr {
 
 // Workgroup size: 1024 threads (16 waves, one kept block each: every K and V
 // load of a head is in flight at once) when the (query, head) workgroups fit
-// in one round on the chip; 512 threads (8 waves, two blocks each, three
-// workgroups per CU) for larger launches, whose 1024-thread workgroups
+// in one round on the chip; 512 threads (8 waves, two blocks each; three
+// workgroups per CU for the fused kernel, two for the plain one) for larger
+// launches, whose 1024-thread workgroups
 // would run in several rounds of one per CU.  Measured on 16 queries: 15.2
 // against 17.3 us; on 64 ragged queries: 31.4 against 41.5 us.
 namespace {
@@ -77,8 +78,15 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
 // kept ids are followed by one memory round trip, the K and V tiles.
 constexpr int kFusedTableCache = 4096;
 
+// The 512-thread variant is held to 80 VGPRs (six waves per SIMD, three
+// workgroups per CU), so a batch's (query, head) workgroups up to three per
+// CU are resident at once (64 ragged queries, 640 workgroups: 34.5 -> 33.4
+// us; at 100 VGPRs two per CU left a second round).  The plain attention
+// kernel measured slower under the same bound (28.6 -> 31.2 us) and keeps
+// its registers.
 template <int NT, int KPT>
-__global__ __launch_bounds__(NT) void select_attn_kernel(SelAttnArgs sa) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 512 ? 6 : 4))) void select_attn_kernel(
+    SelAttnArgs sa) {
   __shared__ SelectSmem<NT> sm;
   __shared__ int32_t s_blocks[kMaxFusedTopk];
   __shared__ int32_t s_table[kFusedTableCache];
