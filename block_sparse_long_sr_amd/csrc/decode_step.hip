@@ -274,9 +274,13 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(WI
           __syncthreads();
           for (int i = tid; i < a.topk; i += kStepThreads) publish(sel_out + i, s_blocks[i]);
           if (a.n_sel != nullptr && tid == 0) a.n_sel[it.slot] = nb < a.topk ? nb : a.topk;
-          drain_stores();
-          __syncthreads();
-          if (tid == 0) count_done(sel_done + it.slot);
+          if (!a.poll_sel) {
+            // the attention items wait for this count (with id polling they
+            // read the ids themselves, and nothing waits for the stores here)
+            drain_stores();
+            __syncthreads();
+            if (tid == 0) count_done(sel_done + it.slot);
+          }
         }
       }
     } else {
@@ -509,6 +513,7 @@ hipError_t launch_decode_step(const DecodeStepArgs& a, const DecodeStepPlan& pla
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t max_cand = (int64_t)a.max_blocks - a.local_blocks;
+  if (max_cand <= kStepThreads * 2 && plan.groups_per_cu == 1) return launch_step<2, true>(a, plan, stream);
   if (max_cand <= kStepThreads * 8) {
     if (plan.groups_per_cu == 1) return launch_step<8, true>(a, plan, stream);
     return launch_step<8, false>(a, plan, stream);
