@@ -259,8 +259,13 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(WI
         drain_stores();
         __syncthreads();
         if (tid == 0) {
+          // the last chunk's workgroup selects.  With one workgroup per CU it
+          // reads the other chunks' scores with device-scope loads and takes
+          // no cache invalidation of its XCD (16 x 12 x 32K: 381-382 ->
+          // 369-377 us); with two, the fence and ordinary loads measured
+          // 0.5% faster (128K: 1073-1079 against 1080-1087 us)
           const bool last = count_done(score_done + it.slot) == (uint32_t)(cb - 1);
-          if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every chunk's scores are visible
+          if (last && !WIDE) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every chunk's scores are visible
           s_last = last;
         }
         __syncthreads();
@@ -268,7 +273,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(WI
           // the slot's scoring is complete: select once for its heads
           const int R = a.topk - a.local_blocks;
           if (!select_trivial(nb, ncand, R, a.topk, s_blocks, kStepThreads))
-            select_sorted_reg<kStepThreads, KPT>(scores, ncand, R, a.local_blocks, s_blocks, sel_sm,
+            select_sorted_reg<kStepThreads, KPT, WIDE>(scores, ncand, R, a.local_blocks, s_blocks, sel_sm,
                                                  a.block_page != nullptr ? a.block_page + (int64_t)b * M : nullptr,
                                                  a.block_page != nullptr ? a.query_page[b] : 0);
           __syncthreads();

@@ -121,7 +121,10 @@ struct SelectSmem {
 // page-aware candidate constraint) a candidate's tier -- 1 when its tag
 // equals `qpage` -- takes the top bit of its ranking key and the score's
 // order key the 31 bits below, so the query's page's blocks rank first.
-template <int NT, int KPT>
+// kCoherent: the scores were written by other workgroups of the same launch
+// (device-scope stores) and are read with device-scope loads, which need no
+// cache invalidation before them.
+template <int NT, int KPT, bool kCoherent = false>
 __device__ __forceinline__ void select_sorted_reg(const float* sc, int ncand, int R, int local_blocks, int32_t* out,
                                                   SelectSmem<NT>& sm, const int32_t* tags = nullptr,
                                                   int32_t qpage = 0) {
@@ -140,7 +143,10 @@ __device__ __forceinline__ void select_sorted_reg(const float* sc, int ncand, in
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int j = tid + i * NT;
-    key[i] = __float_as_uint(sc[j < ncand ? j : ncand - 1]);
+    const float* src = sc + (j < ncand ? j : ncand - 1);
+    key[i] = kCoherent ? __hip_atomic_load(reinterpret_cast<const uint32_t*>(src), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)
+                       : __float_as_uint(*src);
   }
 #pragma unroll
   for (int i = 0; i < KPT; ++i) key[i] = (tid + i * NT < ncand) ? order_key(__uint_as_float(key[i])) : 0u;
